@@ -1,0 +1,375 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+None of these tests re-types an oracle formula and compares it with itself: each compares the
+oracle against a worked example printed on a page, a closed form, an invariant, a brute force,
+or an independent library routine (torch.nn.functional, scipy).
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as Fnn
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def _swiglu_torch(X, wgu, wd):
+    """SwiGLU evaluated with torch.nn.functional in float64 (an independent evaluation)."""
+    X = torch.as_tensor(np.asarray(X, dtype=np.float64))
+    wgu = torch.as_tensor(np.asarray(wgu, dtype=np.float64))
+    wd = torch.as_tensor(np.asarray(wd, dtype=np.float64))
+    F = wgu.shape[0] // 2
+    h = Fnn.silu(Fnn.linear(X, wgu[:F])) * Fnn.linear(X, wgu[F:])
+    return Fnn.linear(h, wd).numpy()
+
+
+def _tiny_layer(rng, T=7, D=8, E=6, F=4, Fs=0, gated=False):
+    x = rng.standard_normal((T, D))
+    wr = rng.standard_normal((E, D))
+    wgu = rng.standard_normal((E, 2 * F, D)) * 0.5
+    wd = rng.standard_normal((E, D, F)) * 0.5
+    extra = {}
+    if Fs:
+        extra["ws_gate_up"] = rng.standard_normal((2 * Fs, D)) * 0.5
+        extra["ws_down"] = rng.standard_normal((D, Fs)) * 0.5
+        extra["w_shared_gate"] = rng.standard_normal((1, D)) if gated else None
+    return x, wr, wgu, wd, extra
+
+
+# ------------------------------------------------------------------------- worked example --
+
+def test_worked_example_routing():
+    g = _golden("worked_example_e5_k2.json")
+    s = np.array(g["scores"])
+    logits = np.log(s / (1.0 - s))[None, :]
+    idx, w = O.route(logits, g["k"], O.SCORING_SIGMOID)
+    assert [i + 1 for i in idx[0]] == g["selected_1based"]
+    np.testing.assert_allclose(w[0], g["weights"], rtol=0, atol=1e-15)
+    assert abs(w[0].sum() - 1.0) <= 1e-15
+
+
+def test_worked_example_output():
+    """y = u + g2·FFN2(u) + g5·FFN5(u); the layer output is everything but the residual u."""
+    g = _golden("worked_example_e5_k2.json")
+    rng = np.random.default_rng(1)
+    D, F, E = 6, 4, g["E"]
+    u = rng.standard_normal((1, D))
+    wgu = rng.standard_normal((E, 2 * F, D))
+    wd = rng.standard_normal((E, D, F))
+    s = np.array(g["scores"])
+    logits = np.log(s / (1.0 - s))[None, :]
+    res = O.moe_forward(u, None, wgu, wd, g["k"], O.SCORING_SIGMOID, logits=logits)
+    y = u + res["out"]
+    e2, e5 = g["selected_1based"][0] - 1, g["selected_1based"][1] - 1
+    expect = (u + g["weights"][0] * _swiglu_torch(u, wgu[e2], wd[e2])
+              + g["weights"][1] * _swiglu_torch(u, wgu[e5], wd[e5]))
+    np.testing.assert_allclose(y, expect, rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------------- top-K --
+
+def _brute_topk_set(keys_row, K):
+    """The unique K-subset whose every member beats every non-member under (key desc, id asc)."""
+    E = len(keys_row)
+    beats = lambda a, b: (keys_row[a] > keys_row[b]) or (keys_row[a] == keys_row[b] and a < b)
+    found = []
+    for S in itertools.combinations(range(E), K):
+        rest = [e for e in range(E) if e not in S]
+        if all(beats(a, b) for a in S for b in rest):
+            found.append(S)
+    assert len(found) == 1
+    S = list(found[0])
+    # slot order: insertion sort under the same order
+    S.sort(key=lambda e: (-keys_row[e], e))
+    return S
+
+
+def _canon(v):
+    return -math.inf if math.isnan(v) else (0.0 if v == 0.0 else v)
+
+
+ADVERSARIAL_ROWS = [
+    [1.0, 1.0, 1.0, 1.0, 1.0, 1.0],
+    [0.5, 2.0, 2.0, -1.0, 2.0, 0.0],
+    [-0.0, 0.0, -0.0, 0.0, -1e-30, 1e-30],
+    [float("nan"), 1.0, float("nan"), -1.0, 0.0, float("nan")],
+    [float("nan")] * 6,
+    [3.0e38, -3.0e38, float("inf"), float("-inf"), 1.0, float("inf")],
+    [float("-inf"), float("nan"), float("-inf"), 0.25, float("nan"), 0.25],
+]
+
+
+@pytest.mark.parametrize("row", ADVERSARIAL_ROWS)
+@pytest.mark.parametrize("K", [1, 2, 3, 6])
+def test_topk_adversarial_vs_brute_force(row, K):
+    idx = O.topk_select(np.array([row]), K)[0]
+    keys = [_canon(v) for v in row]
+    assert list(idx) == _brute_topk_set(keys, K)
+
+
+def test_topk_random_vs_brute_force():
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        E = int(rng.integers(1, 8))
+        K = int(rng.integers(1, E + 1))
+        # quantised values create many exact ties
+        row = rng.integers(-3, 4, size=E).astype(np.float64) * 0.5
+        idx = O.topk_select(row[None, :], K)[0]
+        assert list(idx) == _brute_topk_set(list(row), K)
+
+
+def test_topk_matches_page_shapes():
+    """Router on [2,512,D] tokens with 128 experts, top-8: outputs [2,512,8], rate 8/128."""
+    rng = np.random.default_rng(3)
+    B, S, D, E, K = 2, 512, 16, 128, 8
+    x = rng.standard_normal((B, S, D)).reshape(-1, D)
+    r = O.router_logits(x, rng.standard_normal((E, D)))
+    idx, w = O.route(r, K)
+    assert idx.reshape(B, S, K).shape == (2, 512, 8)
+    assert w.reshape(B, S, K).shape == (2, 512, 8)
+    assert K / E == 0.0625
+
+
+# ---------------------------------------------------------------------- router and gates --
+
+def test_router_logits_pick_columns():
+    """A one-hot token e_j gives r = W_r[:, j]: no transposed operand, no missing term."""
+    rng = np.random.default_rng(11)
+    E, D = 5, 7
+    W = rng.standard_normal((E, D))
+    b = rng.standard_normal(E)
+    x = np.eye(D)
+    np.testing.assert_array_equal(O.router_logits(x, W), W.T)
+    np.testing.assert_allclose(O.router_logits(x, W, b), W.T + b[None, :], rtol=0, atol=0)
+
+
+def test_sigmoid_and_silu_closed_forms():
+    z = np.array([0.0, math.log(3.0), -math.log(3.0), 40.0, -40.0, 800.0, -800.0])
+    s = O.sigmoid(z)
+    assert s[0] == 0.5
+    assert abs(s[1] - 0.75) < 1e-16 and abs(s[2] - 0.25) < 1e-16
+    np.testing.assert_allclose(s, scipy.special.expit(z), rtol=1e-15, atol=0)
+    np.testing.assert_allclose(s + O.sigmoid(-z), 1.0, rtol=0, atol=1e-15)
+    sl = O.silu(z)
+    assert sl[0] == 0.0 and abs(sl[1] - 0.75 * math.log(3.0)) < 1e-15
+    np.testing.assert_allclose(sl, Fnn.silu(torch.as_tensor(z)).numpy(), rtol=1e-14, atol=1e-300)
+
+
+def test_shared_gate_values():
+    x = np.array([[1.0, 0.0], [0.0, 2.0]])
+    w = np.array([[math.log(3.0), 0.5 * math.log(1.0 / 3.0)]])
+    np.testing.assert_allclose(O.shared_gate(x, w), [0.75, 0.25], rtol=0, atol=1e-15)
+
+
+# ------------------------------------------------------------------------------- weights --
+
+@pytest.mark.parametrize("scoring", [O.SCORING_SOFTMAX, O.SCORING_SIGMOID])
+def test_renormalised_weights_sum_to_one(scoring):
+    rng = np.random.default_rng(5)
+    r = rng.standard_normal((50, 32)) * 3
+    for K in (1, 2, 8, 32):
+        idx, w = O.route(r, K, scoring)
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+        assert np.all(w > 0)
+        # weights follow the slot order (both scorings are increasing in r)
+        assert np.all(np.diff(w, axis=1) <= 1e-15)
+
+
+def test_softmax_cancellation_closed_form():
+    """α_k = exp(r_k − r_max)/Σ_{j∈I} exp(r_j − r_max): the full-E denominator cancels."""
+    rng = np.random.default_rng(6)
+    r = rng.standard_normal((40, 64)) * 4
+    idx, w = O.route(r, 6)
+    sel = np.take_along_axis(r, idx.astype(np.int64), axis=1)
+    e = np.exp(sel - sel[:, :1])
+    np.testing.assert_allclose(w, e / e.sum(axis=1, keepdims=True), rtol=1e-13, atol=0)
+
+
+def test_no_renorm_is_full_softmax_and_sigmoid():
+    rng = np.random.default_rng(8)
+    r = rng.standard_normal((20, 16))
+    idx, w = O.route(r, 4, O.SCORING_SOFTMAX, renormalize=False)
+    p = scipy.special.softmax(r, axis=1)
+    np.testing.assert_allclose(w, np.take_along_axis(p, idx.astype(np.int64), 1), rtol=1e-14)
+    assert np.all(w.sum(axis=1) < 1.0)
+    idx, w = O.route(r, 4, O.SCORING_SIGMOID, renormalize=False)
+    np.testing.assert_allclose(
+        w, scipy.special.expit(np.take_along_axis(r, idx.astype(np.int64), 1)), rtol=1e-14)
+
+
+def test_top1_weight_is_one():
+    rng = np.random.default_rng(9)
+    r = rng.standard_normal((30, 9))
+    for scoring in (O.SCORING_SOFTMAX, O.SCORING_SIGMOID):
+        _, w = O.route(r, 1, scoring)
+        assert np.all(w == 1.0)
+
+
+def test_k_equals_e_is_dense_softmax_mixture():
+    rng = np.random.default_rng(10)
+    T, D, E, F = 5, 6, 4, 3
+    x, wr, wgu, wd, _ = _tiny_layer(rng, T=T, D=D, E=E, F=F)
+    res = O.moe_forward(x, wr, wgu, wd, K=E)
+    p = scipy.special.softmax(x @ wr.T, axis=1)
+    dense = sum(p[:, e:e + 1] * _swiglu_torch(x, wgu[e], wd[e]) for e in range(E))
+    np.testing.assert_allclose(res["out"], dense, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------ dispatch --
+
+def _dispatch_by_loops(idx, E):
+    flat = [int(v) for v in np.asarray(idx).reshape(-1)]
+    perm = []
+    counts = []
+    for e in range(E):
+        members = [a for a, v in enumerate(flat) if v == e]
+        counts.append(len(members))
+        perm.extend(members)
+    return counts, perm
+
+
+def test_dispatch_invariants_and_loop_construction():
+    rng = np.random.default_rng(12)
+    for _ in range(20):
+        T, E = int(rng.integers(1, 40)), int(rng.integers(1, 12))
+        K = int(rng.integers(1, E + 1))
+        r = rng.standard_normal((T, E))
+        idx = O.topk_select(r, K)
+        d = O.dispatch(idx, E)
+        counts, perm = _dispatch_by_loops(idx, E)
+        assert list(d["counts"]) == counts
+        assert list(d["perm"]) == perm
+        assert d["counts"].sum() == T * K and d["offsets"][E] == T * K
+        assert d["offsets"][0] == 0 and np.all(np.diff(d["offsets"]) == d["counts"])
+        assert sorted(d["perm"]) == list(range(T * K))
+        np.testing.assert_array_equal(d["inv_perm"][d["perm"]], np.arange(T * K))
+        # within one expert the assignment ids ascend, and every member routes there
+        flat = idx.reshape(-1)
+        for e in range(E):
+            seg = d["perm"][d["offsets"][e]:d["offsets"][e + 1]]
+            assert np.all(np.diff(seg) > 0) and np.all(flat[seg] == e)
+
+
+def test_dispatch_matches_page_count_512():
+    """B=64 tokens at top-8 are 512 dispatches ("S23-J10" §3 worked example 2-4)."""
+    rng = np.random.default_rng(13)
+    idx = O.topk_select(rng.standard_normal((64, 256)), 8)
+    assert O.dispatch(idx, 256)["counts"].sum() == 512
+
+
+def test_dispatch_skips_sentinels():
+    idx = np.array([[0, 3], [3, 9], [-1, 1]])
+    d = O.dispatch(idx, 4)
+    assert list(d["counts"]) == [1, 1, 0, 2]
+    assert list(d["perm"]) == [0, 5, 1, 2]
+    assert list(d["inv_perm"]) == [0, 2, 3, -1, -1, 1]
+
+
+# --------------------------------------------------------------------- experts and layer --
+
+def test_single_expert_layer_is_plain_swiglu():
+    """E=1, K=1 reduces to one SwiGLU MLP, evaluated here with torch.nn.functional."""
+    rng = np.random.default_rng(14)
+    x, wr, wgu, wd, _ = _tiny_layer(rng, T=9, D=8, E=1, F=5)
+    res = O.moe_forward(x, wr, wgu, wd, K=1)
+    np.testing.assert_allclose(res["out"], _swiglu_torch(x, wgu[0], wd[0]), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("scoring", [O.SCORING_SOFTMAX, O.SCORING_SIGMOID])
+@pytest.mark.parametrize("K", [1, 2, 3])
+@pytest.mark.parametrize("shared", [None, "gated", "ungated"])
+def test_sparse_equals_dense_masked_brute_force(scoring, K, shared):
+    rng = np.random.default_rng(15 + K)
+    x, wr, wgu, wd, extra = _tiny_layer(rng, T=11, D=8, E=6, F=4, Fs=3 if shared else 0,
+                                        gated=(shared == "gated"))
+    bias = rng.standard_normal(6)
+    sparse = O.moe_forward(x, wr, wgu, wd, K, scoring, logit_bias=bias, **extra)["out"]
+    dense = O.moe_forward_dense_masked(x, wr, wgu, wd, K, scoring, logit_bias=bias, **extra)
+    np.testing.assert_allclose(sparse, dense, rtol=1e-12, atol=1e-12)
+
+
+def test_shared_branch_gate_and_linearity():
+    rng = np.random.default_rng(16)
+    x, wr, wgu, wd, extra = _tiny_layer(rng, T=10, D=8, E=5, F=4, Fs=6, gated=True)
+    res = O.moe_forward(x, wr, wgu, wd, 2, **extra)
+    branch = res["out"] - res["y_routed"]
+    g = scipy.special.expit(x @ extra["w_shared_gate"].reshape(-1))
+    np.testing.assert_allclose(
+        branch, g[:, None] * _swiglu_torch(x, extra["ws_gate_up"], extra["ws_down"]),
+        rtol=1e-12, atol=1e-12)
+    extra2 = dict(extra, ws_down=2.0 * extra["ws_down"])
+    res2 = O.moe_forward(x, wr, wgu, wd, 2, **extra2)
+    np.testing.assert_allclose(res2["out"] - res2["y_routed"], 2.0 * branch, rtol=1e-12, atol=1e-12)
+    # ungated: g ≡ 1
+    extra3 = dict(extra, w_shared_gate=None)
+    res3 = O.moe_forward(x, wr, wgu, wd, 2, **extra3)
+    np.testing.assert_allclose(res3["out"] - res3["y_routed"],
+                               _swiglu_torch(x, extra["ws_gate_up"], extra["ws_down"]),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_unselected_experts_are_not_evaluated():
+    """Poisoning an expert that no token selects leaves the output unchanged."""
+    rng = np.random.default_rng(17)
+    x, wr, wgu, wd, _ = _tiny_layer(rng, T=6, D=8, E=6, F=4)
+    bias = np.array([0.0, 0.0, -1e9, 0.0, 0.0, 0.0])
+    base = O.moe_forward(x, wr, wgu, wd, 2, logit_bias=bias)["out"]
+    wgu2 = wgu.copy()
+    wgu2[2] = np.nan
+    assert np.array_equal(O.moe_forward(x, wr, wgu2, wd, 2, logit_bias=bias)["out"], base)
+
+
+# ---------------------------------------------------------------------------- cost model --
+
+def test_cost_model_page_numbers():
+    g = _golden("s23_j10_cost_model.json")
+    d, f, k, B = g["d"], g["f"], g["k"], g["B"]
+    assert O.expert_params(d, f) == g["expert_params"]
+    assert 2 * O.expert_params(d, f) == g["expert_bytes_bf16"]
+    # uniform (2 rows on each of 256 experts) and concentrated (64 rows on 8) give equal FLOPs
+    uniform = [2] * 256
+    conc = [64] * 8 + [0] * 248
+    assert O.expert_flops(d, f, uniform) == g["expert_flops_B64_k8"] == O.expert_flops(d, f, conc)
+    assert sum(uniform) == B * k
+    r_uni = O.expert_read_bytes(d, f, 256)
+    r_conc = O.expert_read_bytes(d, f, 8)
+    assert r_uni == g["read_bytes_uniform_U256"] == 1.5 * 2**30
+    assert r_conc == g["read_bytes_concentrated_U8"] == 48 * 2**20
+    assert r_uni // r_conc == g["ratio_uniform_over_concentrated"]
+    assert g["layers"] * r_uni == g["read_bytes_40_layers_uniform"] == 60 * 2**30
+    assert g["layers"] * r_conc == g["read_bytes_40_layers_concentrated"] == 1.875 * 2**30
+    # self-test: B=32, k=8, U=256 still reads 1.5 GiB (U decides, B only changes F)
+    assert O.expert_read_bytes(d, f, 256) == g["self_test_B32_U256_read_bytes"]
+    assert O.expert_params(4096, 2048) == g["v4_flash_expert_params"]
+    assert round(O.expert_flops(d, f, uniform) / 1e9, 2) == 3.22
+
+
+def test_cost_model_granularity_invariance():
+    g = _golden("s23_j10_cost_model.json")
+    (E1, f1, k1), (E2, f2, k2) = g["granularity_pair"]
+    for d in (4096, 2048):
+        assert E1 * O.expert_params(d, f1) == E2 * O.expert_params(d, f2)
+        assert O.expert_flops(d, f1, [k1]) == O.expert_flops(d, f2, [k2])  # one token
+
+
+def test_cost_model_counts_from_dispatch():
+    """Σ t_e from a real dispatch gives F = 2·3·D·F·T·K, and the shared term adds 2·m·N_s."""
+    rng = np.random.default_rng(18)
+    T, E, K, D, F, Fs = 33, 16, 4, 64, 32, 48
+    idx = O.topk_select(rng.standard_normal((T, E)), K)
+    counts = O.dispatch(idx, E)["counts"]
+    assert O.expert_flops(D, F, counts) == 2 * 3 * D * F * T * K
+    assert O.layer_flops(D, F, counts, m=T, f_shared=Fs) == 2 * 3 * D * F * T * K + 6 * D * Fs * T
