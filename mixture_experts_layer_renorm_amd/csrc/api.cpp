@@ -1,0 +1,525 @@
+// Host side of the C ABI declared in include/moe.h: argument validation, workspace layout and
+// the order of kernel launches for each stage.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MOE_HIP_TRY(expr, what)                     \
+  do {                                              \
+    hipError_t e_ = (expr);                         \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t esize(int dtype) { return dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+int check_problem(const moe_problem* p) {
+  if (!p) return fail(MOE_ERR_INVALID_ARG, "problem is NULL");
+  if (p->T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
+  if (p->E < 1) return fail(MOE_ERR_INVALID_ARG, "E < 1");
+  if (p->K < 1 || p->K > p->E) return fail(MOE_ERR_INVALID_ARG, "need 1 <= K <= E (K=%d, E=%d)", p->K, p->E);
+  if (p->D < 1 || p->F < 1 || p->F_shared < 0)
+    return fail(MOE_ERR_INVALID_ARG, "D, F must be positive and F_shared >= 0");
+  if (p->scoring != MOE_SCORE_SOFTMAX && p->scoring != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "unknown scoring %d", p->scoring);
+  if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+  if (p->out_dtype != MOE_DTYPE_F32 && p->out_dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown out_dtype %d", p->out_dtype);
+  if (p->shared_gated != 0 && p->shared_gated != 1)
+    return fail(MOE_ERR_INVALID_ARG, "shared_gated must be 0 or 1");
+  if (p->flags & ~(uint32_t)(MOE_FLAG_DETERMINISTIC | MOE_FLAG_NO_RENORM))
+    return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
+  if (p->D % 64 || p->F % 64 || p->F_shared % 64)
+    return fail(MOE_ERR_UNSUPPORTED, "D, F and F_shared must be multiples of 64 (D=%d F=%d Fs=%d)",
+                p->D, p->F, p->F_shared);
+  if (p->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E > 1024");
+  if (p->K > 64) return fail(MOE_ERR_UNSUPPORTED, "K > 64");
+  if (p->T * (int64_t)p->K >= (int64_t)1 << 31) return fail(MOE_ERR_UNSUPPORTED, "T*K >= 2^31");
+  if (p->T * (int64_t)p->D >= (int64_t)1 << 40) return fail(MOE_ERR_UNSUPPORTED, "T*D too large");
+  return MOE_OK;
+}
+
+bool has_shared(const moe_problem* p) { return p->F_shared > 0; }
+bool gated(const moe_problem* p) { return p->F_shared > 0 && p->shared_gated; }
+
+moe::TileCfg grouped_cfg(const moe_problem* p) {
+  const int64_t A = p->T * p->K;
+  return A <= (int64_t)48 * p->E ? moe::TILE_SMALL : moe::TILE_LARGE;
+}
+moe::TileCfg dense_cfg(int64_t M) { return M <= 256 ? moe::TILE_SMALL : moe::TILE_LARGE; }
+
+// Workspace layout: every region 256-byte aligned.
+struct Layout {
+  size_t logits, gate_logit, gate, topk_idx, topk_w, counts, offsets, perm, inv_perm, seg_counts,
+      tiles, tile_count, H, Hs, acc, y_perm, y_shared, total;
+  int64_t max_mtiles;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Layout layout(const moe_problem* p) {
+  Layout L{};
+  const int64_t T = p->T, A = p->T * p->K, E = p->E, D = p->D;
+  const size_t es = esize(p->dtype);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  L.max_mtiles = (A + 31) / 32 + (E < A ? E : A);  // upper bound for the smallest BM (32)
+  L.logits = take((size_t)T * E * 4);
+  L.gate_logit = take((size_t)T * 4);
+  L.gate = take((size_t)T * 4);
+  L.topk_idx = take((size_t)A * 4);
+  L.topk_w = take((size_t)A * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.perm = take((size_t)A * 4);
+  L.inv_perm = take((size_t)A * 4);
+  L.seg_counts = take((size_t)moe::dispatch_num_segments(A) * E * 4);
+  L.tiles = take((size_t)L.max_mtiles * moe::kTileStride * 4);
+  L.tile_count = take(16);
+  L.H = take((size_t)A * p->F * es);
+  L.Hs = take((size_t)T * p->F_shared * es);
+  L.acc = take((size_t)T * D * 4);
+  if (p->flags & MOE_FLAG_DETERMINISTIC) {
+    L.y_perm = take((size_t)A * D * 4);
+    L.y_shared = take(has_shared(p) ? (size_t)T * D * 4 : 0);
+  } else {
+    L.y_perm = L.y_shared = 0;
+  }
+  L.total = off;
+  return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+int check_ws(const moe_problem* p, void* ws, size_t bytes, Layout* L) {
+  *L = layout(p);
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  if (bytes < L->total)
+    return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", bytes, L->total);
+  return MOE_OK;
+}
+
+#define MOE_CHECK_PTR(ptr, name)                                                    \
+  do {                                                                              \
+    if (!(ptr)) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);                \
+    if (!aligned16(ptr)) return fail(MOE_ERR_INVALID_ARG, "%s not 16-byte aligned", name); \
+  } while (0)
+#define MOE_CHECK_OPT(ptr, name)                                                    \
+  do {                                                                              \
+    if ((ptr) && !aligned16(ptr))                                                   \
+      return fail(MOE_ERR_INVALID_ARG, "%s not 16-byte aligned", name);              \
+  } while (0)
+
+// ---- stage bodies (arguments already validated) -----------------------------------------
+
+hipError_t run_router(const moe_problem* p, const void* x, const moe_weights* w, float* logits,
+                      float* gate_logit, const void* gate_w, hipStream_t s) {
+  const size_t es = esize(p->dtype);
+  moe::GemmParams g{};
+  g.A = (const char*)x;
+  g.lda_bytes = (int64_t)p->D * es;
+  g.B = (const char*)w->w_router;
+  g.ldb_bytes = (int64_t)p->D * es;
+  g.B2 = (const char*)gate_w;
+  g.N = p->E;
+  g.Kdim = p->D;
+  g.M = (int32_t)p->T;
+  g.C = logits;
+  g.ldc = p->E;
+  g.C2 = gate_logit;
+  g.col_bias = w->logit_bias;
+  const moe::TileCfg cfg = dense_cfg(p->T);
+  const int bm = moe::tile_bm(cfg);
+  return moe::launch_gemm(p->dtype, cfg, moe::EPI_STORE, g, (p->T + bm - 1) / bm, s);
+}
+
+// gate_up over the tile map: rows gathered from x through perm (or read from x_perm).
+hipError_t run_gate_up(const moe_problem* p, const void* x, const void* x_perm, const void* w_gu,
+                       const int32_t* perm, const int32_t* tiles, const int32_t* tile_count,
+                       int64_t max_mtiles, void* H, moe::TileCfg cfg, hipStream_t s) {
+  const size_t es = esize(p->dtype);
+  moe::GemmParams g{};
+  g.A = (const char*)(x_perm ? x_perm : x);
+  g.lda_bytes = (int64_t)p->D * es;
+  g.a_gather = x_perm ? nullptr : perm;
+  g.a_div = p->K;
+  g.B = (const char*)w_gu;
+  g.b_group_bytes = (int64_t)2 * p->F * p->D * es;
+  g.ldb_bytes = (int64_t)p->D * es;
+  g.N = p->F;
+  g.Kdim = p->D;
+  g.tiles = tiles;
+  g.tile_count = tile_count;
+  g.C = H;
+  g.ldc = p->F;
+  return moe::launch_gemm(p->dtype, cfg, moe::EPI_SWIGLU, g, max_mtiles, s);
+}
+
+hipError_t run_down(const moe_problem* p, const void* H, const void* w_d, const int32_t* tiles,
+                    const int32_t* tile_count, int64_t max_mtiles, moe::TileCfg cfg,
+                    float* y_perm, float* acc, const int32_t* perm, const float* topk_w,
+                    hipStream_t s) {
+  const size_t es = esize(p->dtype);
+  moe::GemmParams g{};
+  g.A = (const char*)H;
+  g.lda_bytes = (int64_t)p->F * es;
+  g.B = (const char*)w_d;
+  g.b_group_bytes = (int64_t)p->D * p->F * es;
+  g.ldb_bytes = (int64_t)p->F * es;
+  g.N = p->D;
+  g.Kdim = p->F;
+  g.tiles = tiles;
+  g.tile_count = tile_count;
+  if (y_perm) {
+    g.C = y_perm;
+    g.ldc = p->D;
+    return moe::launch_gemm(p->dtype, cfg, moe::EPI_STORE, g, max_mtiles, s);
+  }
+  g.acc_out = acc;
+  g.ldo = p->D;
+  g.perm = perm;
+  g.topk_w = topk_w;
+  g.topk = p->K;
+  return moe::launch_gemm(p->dtype, cfg, moe::EPI_ATOMIC_COMBINE, g, max_mtiles, s);
+}
+
+// Shared expert on all T tokens: Hs = SwiGLU gate/up of x; out = row_scale * (Hs Ws_downᵀ).
+hipError_t run_shared(const moe_problem* p, const void* x, const moe_weights* w, void* Hs,
+                      float* out, const float* row_scale, hipStream_t s) {
+  const size_t es = esize(p->dtype);
+  const moe::TileCfg cfg = dense_cfg(p->T);
+  const int bm = moe::tile_bm(cfg);
+  const int64_t mt = (p->T + bm - 1) / bm;
+  moe::GemmParams g{};
+  g.A = (const char*)x;
+  g.lda_bytes = (int64_t)p->D * es;
+  g.B = (const char*)w->ws_gate_up;
+  g.ldb_bytes = (int64_t)p->D * es;
+  g.N = p->F_shared;
+  g.Kdim = p->D;
+  g.M = (int32_t)p->T;
+  g.C = Hs;
+  g.ldc = p->F_shared;
+  hipError_t e = moe::launch_gemm(p->dtype, cfg, moe::EPI_SWIGLU, g, mt, s);
+  if (e != hipSuccess) return e;
+  moe::GemmParams d{};
+  d.A = (const char*)Hs;
+  d.lda_bytes = (int64_t)p->F_shared * es;
+  d.B = (const char*)w->ws_down;
+  d.ldb_bytes = (int64_t)p->F_shared * es;
+  d.N = p->D;
+  d.Kdim = p->F_shared;
+  d.M = (int32_t)p->T;
+  d.C = out;
+  d.ldc = p->D;
+  d.row_scale = row_scale;
+  return moe::launch_gemm(p->dtype, cfg, moe::EPI_STORE, d, mt, s);
+}
+
+int check_weights(const moe_problem* p, const moe_weights* w, bool router, bool experts) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  if (router) {
+    MOE_CHECK_PTR(w->w_router, "w_router");
+    MOE_CHECK_OPT(w->logit_bias, "logit_bias");
+    if (gated(p)) MOE_CHECK_PTR(w->ws_gate, "ws_gate");
+  }
+  if (experts) {
+    MOE_CHECK_PTR(w->w_gate_up, "w_gate_up");
+    MOE_CHECK_PTR(w->w_down, "w_down");
+    if (has_shared(p)) {
+      MOE_CHECK_PTR(w->ws_gate_up, "ws_gate_up");
+      MOE_CHECK_PTR(w->ws_down, "ws_down");
+    }
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_workspace_size(const moe_problem* p, size_t* bytes) {
+  g_last_error.clear();
+  int st = check_problem(p);
+  if (st) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = layout(p).total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_problem* p, const void* x, const moe_weights* w, moe_routing* r,
+              void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  g_last_error.clear();
+  int st = check_problem(p);
+  if (st) return st;
+  if (p->T == 0) return MOE_OK;
+  MOE_CHECK_PTR(x, "x");
+  if ((st = check_weights(p, w, true, false))) return st;
+  if (!r) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
+  MOE_CHECK_PTR(r->topk_idx, "topk_idx");
+  MOE_CHECK_PTR(r->topk_w, "topk_w");
+  MOE_CHECK_OPT(r->logits, "logits");
+  MOE_CHECK_OPT(r->shared_gate, "shared_gate");
+  Layout L;
+  if ((st = check_ws(p, workspace, workspace_bytes, &L))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  float* logits = r->logits ? r->logits : at<float>(workspace, L.logits);
+  const bool want_gate = gated(p) && r->shared_gate;
+  float* gate_logit = at<float>(workspace, L.gate_logit);
+  MOE_HIP_TRY(run_router(p, x, w, logits, want_gate ? gate_logit : nullptr,
+                         want_gate ? w->ws_gate : nullptr, s),
+              "router GEMM launch");
+  MOE_HIP_TRY(moe::launch_topk(logits, p->T, p->E, p->K, p->scoring,
+                               !(p->flags & MOE_FLAG_NO_RENORM), r->topk_idx, r->topk_w,
+                               want_gate ? gate_logit : nullptr,
+                               want_gate ? r->shared_gate : nullptr, s),
+              "top-K launch");
+  return MOE_OK;
+}
+
+int moe_route_logits(const moe_problem* p, const float* logits, moe_routing* r,
+                     moe_stream_t stream) {
+  g_last_error.clear();
+  int st = check_problem(p);
+  if (st) return st;
+  if (p->T == 0) return MOE_OK;
+  MOE_CHECK_PTR(logits, "logits");
+  if (!r) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
+  MOE_CHECK_PTR(r->topk_idx, "topk_idx");
+  MOE_CHECK_PTR(r->topk_w, "topk_w");
+  MOE_HIP_TRY(moe::launch_topk(logits, p->T, p->E, p->K, p->scoring,
+                               !(p->flags & MOE_FLAG_NO_RENORM), r->topk_idx, r->topk_w, nullptr,
+                               nullptr, (hipStream_t)stream),
+              "top-K launch");
+  return MOE_OK;
+}
+
+int moe_dispatch(const moe_problem* p, const void* x, moe_routing* r, void* x_perm,
+                 void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  g_last_error.clear();
+  int st = check_problem(p);
+  if (st) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!r) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
+  MOE_CHECK_PTR(r->topk_idx, "topk_idx");
+  MOE_CHECK_PTR(r->expert_counts, "expert_counts");
+  MOE_CHECK_PTR(r->expert_offsets, "expert_offsets");
+  MOE_CHECK_PTR(r->perm, "perm");
+  MOE_CHECK_PTR(r->inv_perm, "inv_perm");
+  MOE_CHECK_OPT(x_perm, "x_perm");
+  if (x_perm) MOE_CHECK_PTR(x, "x");
+  Layout L;
+  if ((st = check_ws(p, workspace, workspace_bytes, &L))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t A = p->T * p->K;
+  MOE_HIP_TRY(moe::launch_dispatch(r->topk_idx, A, p->E, at<int32_t>(workspace, L.seg_counts),
+                                   r->expert_counts, r->expert_offsets, r->perm, r->inv_perm, 32,
+                                   nullptr, nullptr, s),
+              "dispatch launch");
+  if (x_perm)
+    MOE_HIP_TRY(moe::launch_gather_rows(x, p->D, (int)esize(p->dtype), r->perm, r->expert_offsets,
+                                        p->E, p->K, A, x_perm, s),
+                "row gather launch");
+  return MOE_OK;
+}
+
+int moe_experts(const moe_problem* p, const void* x, const void* x_perm, const moe_weights* w,
+                const moe_routing* r, float* y_perm, float* y_shared, void* workspace,
+                size_t workspace_bytes, moe_stream_t stream) {
+  g_last_error.clear();
+  int st = check_problem(p);
+  if (st) return st;
+  if (p->T == 0) return MOE_OK;
+  if ((st = check_weights(p, w, false, true))) return st;
+  if (!x && !x_perm) return fail(MOE_ERR_INVALID_ARG, "x and x_perm are both NULL");
+  MOE_CHECK_OPT(x, "x");
+  MOE_CHECK_OPT(x_perm, "x_perm");
+  if (has_shared(p) && y_shared) MOE_CHECK_PTR(x, "x");
+  if (!r) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
+  MOE_CHECK_PTR(r->expert_offsets, "expert_offsets");
+  if (!x_perm) MOE_CHECK_PTR(r->perm, "perm");
+  MOE_CHECK_PTR(y_perm, "y_perm");
+  MOE_CHECK_OPT(y_shared, "y_shared");
+  Layout L;
+  if ((st = check_ws(p, workspace, workspace_bytes, &L))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const moe::TileCfg cfg = grouped_cfg(p);
+  const int bm = moe::tile_bm(cfg);
+  int32_t* tiles = at<int32_t>(workspace, L.tiles);
+  int32_t* tile_count = at<int32_t>(workspace, L.tile_count);
+  MOE_HIP_TRY(moe::launch_tile_map(r->expert_offsets, p->E, bm, tiles, tile_count, s),
+              "tile map launch");
+  void* H = at<void>(workspace, L.H);
+  MOE_HIP_TRY(run_gate_up(p, x, x_perm, w->w_gate_up, r->perm, tiles, tile_count, L.max_mtiles, H,
+                          cfg, s),
+              "gate_up GEMM launch");
+  MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, cfg, y_perm, nullptr,
+                       nullptr, nullptr, s),
+              "down GEMM launch");
+  if (has_shared(p) && y_shared)
+    MOE_HIP_TRY(run_shared(p, x, w, at<void>(workspace, L.Hs), y_shared, nullptr, s),
+                "shared expert launch");
+  return MOE_OK;
+}
+
+int moe_combine(const moe_problem* p, const float* y_perm, const moe_routing* r,
+                const float* y_shared, void* out, moe_stream_t stream) {
+  g_last_error.clear();
+  int st = check_problem(p);
+  if (st) return st;
+  if (p->T == 0) return MOE_OK;
+  MOE_CHECK_PTR(y_perm, "y_perm");
+  MOE_CHECK_PTR(out, "out");
+  MOE_CHECK_OPT(y_shared, "y_shared");
+  if (!r) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
+  MOE_CHECK_PTR(r->inv_perm, "inv_perm");
+  MOE_CHECK_PTR(r->topk_w, "topk_w");
+  const float* gate = nullptr;
+  if (y_shared && gated(p)) {
+    MOE_CHECK_PTR(r->shared_gate, "shared_gate");
+    gate = r->shared_gate;
+  }
+  MOE_HIP_TRY(moe::launch_combine(y_perm, r->inv_perm, r->topk_w, has_shared(p) ? y_shared : nullptr,
+                                  gate, p->T, p->K, p->D, out, p->out_dtype, (hipStream_t)stream),
+              "combine launch");
+  return MOE_OK;
+}
+
+int moe_forward(const moe_problem* p, const void* x, const moe_weights* w, moe_routing* r_opt,
+                void* out, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  g_last_error.clear();
+  int st = check_problem(p);
+  if (st) return st;
+  if (p->T == 0) return MOE_OK;
+  MOE_CHECK_PTR(x, "x");
+  MOE_CHECK_PTR(out, "out");
+  if (out == x) return fail(MOE_ERR_INVALID_ARG, "out aliases x");
+  if ((st = check_weights(p, w, true, true))) return st;
+  moe_routing r{};
+  if (r_opt) {
+    r = *r_opt;
+    MOE_CHECK_OPT(r.logits, "logits");
+    MOE_CHECK_OPT(r.topk_idx, "topk_idx");
+    MOE_CHECK_OPT(r.topk_w, "topk_w");
+    MOE_CHECK_OPT(r.expert_counts, "expert_counts");
+    MOE_CHECK_OPT(r.expert_offsets, "expert_offsets");
+    MOE_CHECK_OPT(r.perm, "perm");
+    MOE_CHECK_OPT(r.inv_perm, "inv_perm");
+    MOE_CHECK_OPT(r.shared_gate, "shared_gate");
+  }
+  Layout L;
+  if ((st = check_ws(p, workspace, workspace_bytes, &L))) return st;
+  void* ws = workspace;
+  if (!r.logits) r.logits = at<float>(ws, L.logits);
+  if (!r.topk_idx) r.topk_idx = at<int32_t>(ws, L.topk_idx);
+  if (!r.topk_w) r.topk_w = at<float>(ws, L.topk_w);
+  if (!r.expert_counts) r.expert_counts = at<int32_t>(ws, L.counts);
+  if (!r.expert_offsets) r.expert_offsets = at<int32_t>(ws, L.offsets);
+  if (!r.perm) r.perm = at<int32_t>(ws, L.perm);
+  if (!r.inv_perm) r.inv_perm = at<int32_t>(ws, L.inv_perm);
+  if (!r.shared_gate) r.shared_gate = at<float>(ws, L.gate);
+
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t A = p->T * p->K;
+  const bool g = gated(p);
+  float* gate_logit = at<float>(ws, L.gate_logit);
+
+  // 1. router GEMM (+ shared-gate column) and top-K
+  MOE_HIP_TRY(run_router(p, x, w, r.logits, g ? gate_logit : nullptr, g ? w->ws_gate : nullptr, s),
+              "router GEMM launch");
+  MOE_HIP_TRY(moe::launch_topk(r.logits, p->T, p->E, p->K, p->scoring,
+                               !(p->flags & MOE_FLAG_NO_RENORM), r.topk_idx, r.topk_w,
+                               g ? gate_logit : nullptr, g ? r.shared_gate : nullptr, s),
+              "top-K launch");
+  // 2. dispatch + tile map
+  const moe::TileCfg cfg = grouped_cfg(p);
+  const int bm = moe::tile_bm(cfg);
+  int32_t* tiles = at<int32_t>(ws, L.tiles);
+  int32_t* tile_count = at<int32_t>(ws, L.tile_count);
+  MOE_HIP_TRY(moe::launch_dispatch(r.topk_idx, A, p->E, at<int32_t>(ws, L.seg_counts),
+                                   r.expert_counts, r.expert_offsets, r.perm, r.inv_perm, bm, tiles,
+                                   tile_count, s),
+              "dispatch launch");
+  // 3. routed gate_up with SiLU*up
+  void* H = at<void>(ws, L.H);
+  MOE_HIP_TRY(run_gate_up(p, x, nullptr, w->w_gate_up, r.perm, tiles, tile_count, L.max_mtiles, H,
+                          cfg, s),
+              "gate_up GEMM launch");
+  const float* gate = g ? r.shared_gate : nullptr;
+  if (p->flags & MOE_FLAG_DETERMINISTIC) {
+    float* y_perm = at<float>(ws, L.y_perm);
+    float* y_shared = has_shared(p) ? at<float>(ws, L.y_shared) : nullptr;
+    MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, cfg, y_perm, nullptr,
+                         nullptr, nullptr, s),
+                "down GEMM launch");
+    if (y_shared)
+      MOE_HIP_TRY(run_shared(p, x, w, at<void>(ws, L.Hs), y_shared, nullptr, s),
+                  "shared expert launch");
+    MOE_HIP_TRY(moe::launch_combine(y_perm, r.inv_perm, r.topk_w, y_shared, gate, p->T, p->K,
+                                    p->D, out, p->out_dtype, s),
+                "combine launch");
+    return MOE_OK;
+  }
+  // 4. fp32 accumulator: the shared branch initialises it (or it is zeroed), then the down
+  //    GEMM adds the weighted routed rows with atomics, then one cast to the output dtype.
+  float* acc = p->out_dtype == MOE_DTYPE_F32 ? static_cast<float*>(out) : at<float>(ws, L.acc);
+  if (has_shared(p))
+    MOE_HIP_TRY(run_shared(p, x, w, at<void>(ws, L.Hs), acc, gate, s), "shared expert launch");
+  else
+    MOE_HIP_TRY(moe::launch_zero(acc, p->T * p->D, s), "zero launch");
+  MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, cfg, nullptr, acc, r.perm,
+                       r.topk_w, s),
+              "down GEMM launch");
+  if (p->out_dtype != MOE_DTYPE_F32)
+    MOE_HIP_TRY(moe::launch_cast(acc, out, p->T * p->D, p->out_dtype, s), "cast launch");
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// Combine and output conversion ("MoE" §3.2: weighted rows are accumulated back at their
+// tokens; §4: the routed and shared branches are added).
+//
+// combine : deterministic gather-sum.  One work-group per token: the K rows of the token's
+//           expert outputs are read through inv_perm and summed in slot order in fp32, the
+//           shared branch is added with its gate, and the sum is rounded once to the output
+//           dtype.  16-byte loads along D.
+// cast    : fp32 accumulator -> output dtype (round to nearest even), for the atomic path.
+// zero    : fill an fp32 accumulator with +0.0 (a kernel, not a memset node).
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ void store4(float* dst, float4 v) { *(float4*)dst = v; }
+__device__ __forceinline__ void store4(__bf16* dst, float4 v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 o;
+  o[0] = (__bf16)v.x;
+  o[1] = (__bf16)v.y;
+  o[2] = (__bf16)v.z;
+  o[3] = (__bf16)v.w;
+  *(bf16x4*)dst = o;
+}
+
+template <typename OUT>
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ y_perm,
+                                                      const int32_t* __restrict__ inv_perm,
+                                                      const float* __restrict__ topk_w,
+                                                      const float* __restrict__ y_shared,
+                                                      const float* __restrict__ gate, int64_t T,
+                                                      int K, int D, OUT* __restrict__ out) {
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    const float g = y_shared ? (gate ? gate[t] : 1.0f) : 0.0f;
+    for (int d = threadIdx.x * 4; d < D; d += blockDim.x * 4) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < K; ++k) {
+        const int pos = inv_perm[t * K + k];
+        if (pos < 0) continue;  // sentinel assignment
+        const float w = topk_w[t * K + k];
+        const float4 v = *(const float4*)(y_perm + (int64_t)pos * D + d);
+        acc.x += w * v.x;
+        acc.y += w * v.y;
+        acc.z += w * v.z;
+        acc.w += w * v.w;
+      }
+      if (y_shared) {
+        const float4 v = *(const float4*)(y_shared + t * D + d);
+        acc.x += g * v.x;
+        acc.y += g * v.y;
+        acc.z += g * v.z;
+        acc.w += g * v.w;
+      }
+      store4(out + t * D + d, acc);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) cast_bf16_kernel(const float* __restrict__ src,
+                                                        __bf16* __restrict__ dst, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x)
+    store4(dst + 4 * i, ((const float4*)src)[i]);
+}
+
+__global__ void __launch_bounds__(256) zero_kernel(float4* __restrict__ dst, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+unsigned grid_for(int64_t n4) {
+  int64_t g = (n4 + 255) / 256;
+  const int64_t cap = (int64_t)kCus * 8;
+  return (unsigned)(g < 1 ? 1 : (g > cap ? cap : g));
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
+                          const float* y_shared, const float* gate, int64_t T, int K, int D,
+                          void* out, int out_dtype, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  const int64_t cap = (int64_t)kCus * 16;
+  const dim3 g((unsigned)(T < cap ? T : cap)), b(256);
+  if (out_dtype == 1)
+    hipLaunchKernelGGL(combine_kernel<__bf16>, g, b, 0, stream, y_perm, inv_perm, topk_w, y_shared,
+                       gate, T, K, D, (__bf16*)out);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, g, b, 0, stream, y_perm, inv_perm, topk_w, y_shared,
+                       gate, T, K, D, (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast(const float* src, void* dst, int64_t n, int out_dtype, hipStream_t stream) {
+  if (n <= 0 || out_dtype != 1) return hipSuccess;
+  const int64_t n4 = n / 4;  // n = T*D, D % 64 == 0
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid_for(n4)), dim3(256), 0, stream, src, (__bf16*)dst,
+                     n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(float* dst, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t n4 = n / 4;
+  hipLaunchKernelGGL(zero_kernel, dim3(grid_for(n4)), dim3(256), 0, stream, (float4*)dst, n4);
+  return hipGetLastError();
+}
+
+}  // namespace moe

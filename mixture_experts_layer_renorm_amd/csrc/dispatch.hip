@@ -1,0 +1,307 @@
+// Dispatch: per-expert histogram, prefix sum and a stable counting sort of the T*K assignments
+// into expert-contiguous order ("MoE" §3.2: the tokens routed to each hit expert are gathered so
+// that the expert runs once on all of them; "1.6 混合专家（MoE）" §二: route, group, compute,
+// merge).
+//
+// The assignments a = t*K + k are cut into segments of 1024 consecutive ids, one wave64 each
+// (each lane prefetches its 16 ids of the segment at once).
+//   count   : each wave histograms its segment in LDS (atomics are fine: counts do not depend
+//             on order) and writes seg_counts[segment][E].
+//   scan    : one work-group scans seg_counts expert-major (expert, then segment), giving every
+//             (segment, expert) pair its first output position, the expert counts and offsets,
+//             and the grouped-GEMM tile map.
+//   scatter : each wave re-reads its segment 64 ids at a time.  Lanes holding the same expert
+//             find each other with one ballot per bit of the expert id; a lane's rank among its
+//             lower-numbered peers plus the running position of its expert (in LDS) is its
+//             output position.  Segments, rounds and lanes all follow ascending a, so the sort
+//             is stable and the result bit-exact.
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kScanThreads = 1024;
+constexpr int kSegRounds = 16;               // 64-id rounds per segment
+constexpr int kSegLen = 64 * kSegRounds;      // assignments per segment (one wave)
+
+__device__ __forceinline__ int wave_prefix_exclusive(int v, int lane) {
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x - v;
+}
+
+// Exclusive scan of one int per thread across a 1024-thread block.  Returns the prefix and
+// writes the block total to *total.
+__device__ int block_exclusive_scan(int v, int* scratch /* >= 17 ints */, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ex = wave_prefix_exclusive(v, lane);
+  if (lane == 63) scratch[wave] = ex + v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      const int c = scratch[w];
+      scratch[w] = run;
+      run += c;
+    }
+    scratch[kScanThreads / 64] = run;
+  }
+  __syncthreads();
+  const int r = ex + scratch[wave];
+  *total = scratch[kScanThreads / 64];
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(256) count_kernel(const int32_t* __restrict__ idx, int64_t A,
+                                                    int E, int64_t nseg,
+                                                    int32_t* __restrict__ seg_counts) {
+  extern __shared__ int hist_all[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t seg = (int64_t)blockIdx.x * 4 + wave;
+  if (seg >= nseg) return;  // whole wave; no block-wide barrier below
+  int* hist = hist_all + wave * E;
+  for (int e = lane; e < E; e += 64) hist[e] = 0;
+  const int64_t a0 = seg * kSegLen;
+  int ev[kSegRounds];
+#pragma unroll
+  for (int r = 0; r < kSegRounds; ++r) {
+    const int64_t a = a0 + r * 64 + lane;
+    ev[r] = a < A ? idx[a] : -1;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int r = 0; r < kSegRounds; ++r)
+    if (ev[r] >= 0 && ev[r] < E) atomicAdd(&hist[ev[r]], 1);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  for (int e = lane; e < E; e += 64) seg_counts[seg * E + e] = hist[e];
+}
+
+// Builds the tile map from per-expert counts held in LDS.  One entry per M tile:
+// {expert, first row position, rows, 0, first M tile of the expert, M tiles of the expert}.
+__device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, int bm, int* scratch,
+                            int32_t* tiles, int32_t* tile_count) {
+  int total = 0;
+  for (int base = 0; base < E; base += kScanThreads) {
+    const int e = base + threadIdx.x;
+    const int c = e < E ? cnt_lds[e] : 0;
+    const int mt = (c + bm - 1) / bm;
+    int chunk_total;
+    const int first = block_exclusive_scan(mt, scratch, &chunk_total) + total;
+    if (e < E) {
+      for (int q = 0; q < mt; ++q) {
+        int32_t* ent = tiles + (int64_t)(first + q) * kTileStride;
+        ent[0] = e;
+        ent[1] = off_lds[e] + q * bm;
+        ent[2] = min(bm, c - q * bm);
+        ent[3] = 0;
+        ent[4] = first;
+        ent[5] = mt;
+        ent[6] = 0;
+        ent[7] = 0;
+      }
+    }
+    total += chunk_total;
+  }
+  if (threadIdx.x == 0) *tile_count = total;
+}
+
+__global__ void __launch_bounds__(kScanThreads) scan_kernel(int32_t* __restrict__ seg_counts,
+                                                            int64_t nseg, int E,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets, int bm,
+                                                            int32_t* __restrict__ tiles,
+                                                            int32_t* __restrict__ tile_count) {
+  extern __shared__ int sm[];
+  int* cnt = sm;             // [E]
+  int* off = sm + E;         // [E]
+  int* part = sm + 2 * E;    // [kScanThreads]
+  int* scratch = part + kScanThreads;  // [17]
+  // Threads are (chunk c, expert e); P chunks per expert split the segments.  E <= 1024.
+  int ep = 1;
+  while (ep < E) ep <<= 1;
+  const int P = kScanThreads / ep;
+  const int e = threadIdx.x % ep, c = threadIdx.x / ep;
+  const int64_t per = (nseg + P - 1) / P;
+  const int64_t s0 = (int64_t)c * per, s1 = min(nseg, s0 + per);
+  const bool active = e < E;
+  int sum = 0;
+  if (active) {
+    for (int64_t s = s0; s < s1; s += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = s + u < s1 ? seg_counts[(s + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) sum += v[u];
+    }
+  }
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  if (active) {
+    int run = 0;
+    for (int cc = 0; cc < c; ++cc) run += part[cc * ep + e];
+    for (int64_t s = s0; s < s1; s += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = s + u < s1 ? seg_counts[(s + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (s + u < s1) seg_counts[(s + u) * E + e] = run;  // the segment's base in expert e
+        run += v[u];
+      }
+    }
+    if (c == P - 1) cnt[e] = run;
+  }
+  __syncthreads();
+  // expert offsets
+  int total = 0;
+  for (int base = 0; base < E; base += kScanThreads) {
+    const int ee = base + threadIdx.x;
+    const int v = ee < E ? cnt[ee] : 0;
+    int chunk_total;
+    const int ex = block_exclusive_scan(v, scratch, &chunk_total) + total;
+    if (ee < E) {
+      off[ee] = ex;
+      counts[ee] = v;
+      offsets[ee] = ex;
+    }
+    total += chunk_total;
+  }
+  if (threadIdx.x == 0) offsets[E] = total;
+  __syncthreads();
+  if (tiles) build_tiles(cnt, off, E, bm, scratch, tiles, tile_count);
+}
+
+__global__ void __launch_bounds__(kScanThreads) tile_map_kernel(const int32_t* __restrict__ offsets,
+                                                                int E, int bm,
+                                                                int32_t* __restrict__ tiles,
+                                                                int32_t* __restrict__ tile_count) {
+  extern __shared__ int sm[];
+  int* cnt = sm;
+  int* off = sm + E;
+  int* scratch = sm + 2 * E;
+  for (int e = threadIdx.x; e < E; e += kScanThreads) {
+    off[e] = offsets[e];
+    cnt[e] = offsets[e + 1] - offsets[e];
+  }
+  __syncthreads();
+  build_tiles(cnt, off, E, bm, scratch, tiles, tile_count);
+}
+
+__global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ idx, int64_t A,
+                                                      int E, int nbits, int64_t nseg,
+                                                      const int32_t* __restrict__ seg_base,
+                                                      const int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ perm,
+                                                      int32_t* __restrict__ inv_perm) {
+  extern __shared__ int run_all[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t seg = (int64_t)blockIdx.x * 4 + wave;
+  if (seg >= nseg) return;
+  int* run = run_all + wave * E;
+  const int64_t a0 = seg * kSegLen;
+  int ev[kSegRounds];
+#pragma unroll
+  for (int r = 0; r < kSegRounds; ++r) {
+    const int64_t a = a0 + r * 64 + lane;
+    ev[r] = a < A ? idx[a] : -1;
+  }
+  for (int e = lane; e < E; e += 64) run[e] = offsets[e] + seg_base[seg * E + e];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int r = 0; r < kSegRounds; ++r) {
+    const int64_t a = a0 + r * 64 + lane;
+    const int e = ev[r];
+    const bool valid = e >= 0 && e < E;
+    unsigned long long peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const unsigned long long m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    if (valid) {
+      const int rank = __popcll(peers & lt);
+      const int base = run[e];
+      const int pos = base + rank;
+      perm[pos] = (int32_t)a;
+      inv_perm[a] = pos;
+      if (rank == 0) run[e] = base + __popcll(peers);
+    } else if (a < A) {
+      inv_perm[a] = -1;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <typename V>
+__global__ void __launch_bounds__(256) gather_rows_kernel(const V* __restrict__ x, int64_t vrow,
+                                                          const int32_t* __restrict__ perm,
+                                                          const int32_t* __restrict__ offsets,
+                                                          int E, int K, int64_t A,
+                                                          V* __restrict__ x_perm) {
+  const int64_t valid = offsets[E];
+  for (int64_t pos = blockIdx.x; pos < valid; pos += gridDim.x) {
+    const int64_t tok = perm[pos] / K;
+    const V* src = x + tok * vrow;
+    V* dst = x_perm + pos * vrow;
+    for (int64_t c = threadIdx.x; c < vrow; c += blockDim.x) dst[c] = src[c];
+  }
+}
+
+}  // namespace
+
+int dispatch_segment_len(int64_t) { return kSegLen; }
+
+int64_t dispatch_num_segments(int64_t A) { return (A + kSegLen - 1) / kSegLen; }
+
+hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_counts,
+                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                           int bm, int32_t* tiles, int32_t* tile_count, hipStream_t stream) {
+  const int64_t nseg = dispatch_num_segments(A);
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  const dim3 g((unsigned)((nseg + 3) / 4)), b(256);
+  const size_t lds_waves = (size_t)4 * E * sizeof(int);
+  hipLaunchKernelGGL(count_kernel, g, b, lds_waves, stream, idx, A, E, nseg, seg_counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t lds_scan = (size_t)(2 * E + kScanThreads + 32) * sizeof(int);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), lds_scan, stream, seg_counts, nseg,
+                     E, counts, offsets, bm, tiles, tile_count);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(scatter_kernel, g, b, lds_waves, stream, idx, A, E, nbits, nseg, seg_counts,
+                     offsets, perm, inv_perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_map(const int32_t* offsets, int E, int bm, int32_t* tiles,
+                           int32_t* tile_count, hipStream_t stream) {
+  const size_t lds = (size_t)(2 * E + 32) * sizeof(int);
+  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(kScanThreads), lds, stream, offsets, E, bm,
+                     tiles, tile_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, int64_t D, int esize, const int32_t* perm,
+                              const int32_t* offsets, int E, int K, int64_t A, void* x_perm,
+                              hipStream_t stream) {
+  if (A <= 0) return hipSuccess;
+  const int64_t row_bytes = D * esize;  // multiple of 128 (D % 64 == 0)
+  const int64_t vrow = row_bytes / 16;
+  const int64_t grid = A < 4096 ? A : 4096;
+  hipLaunchKernelGGL(gather_rows_kernel<uint4>, dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const uint4*)x, vrow, perm, offsets, E, K, A, (uint4*)x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,88 @@
+// Internal declarations shared by the HIP translation units and the host API layer.
+// Nothing here is part of the public ABI (include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kXcds = 8;         // MI355X: 8 accelerator complex dies, 32 CUs each
+constexpr int kCus = 256;
+constexpr int kTileStride = 8;   // int32 words per tile-map entry
+
+// Grouped / dense GEMM description.  C[row, n] = sum_k A[row, k] * B[n, k]; rows come from
+// per-group row ranges (tile map) or one dense range [0, M).
+enum Epilogue : int {
+  EPI_STORE = 0,           // fp32 store (+ column bias, x row scale); column N goes to C2
+  EPI_SWIGLU = 1,          // H[row, n] = SiLU(C[row, n]) * C[row, F + n], stored in dtype
+  EPI_ATOMIC_COMBINE = 2,  // out_acc[token(row), n] += w(row) * C[row, n]  (fp32 atomics)
+};
+
+struct GemmParams {
+  // A operand: row r of the logical A matrix is A + arow(r) * lda_bytes.
+  const char* A;
+  int64_t lda_bytes;
+  const int32_t* a_gather;  // if non-null: arow(pos) = a_gather[pos] / a_div
+  int32_t a_div;
+  // B operand: [groups][rows][Kdim]; group stride in bytes.
+  const char* B;
+  int64_t b_group_bytes;
+  int64_t ldb_bytes;
+  const char* B2;           // optional extra B row, output column N (router's shared-gate column)
+  int32_t N;                // output columns per group (SWIGLU: F, B has 2F rows)
+  int32_t Kdim;             // reduction length, elements
+  // Tiles: map mode (tiles != null) or dense mode over M rows.
+  const int32_t* tiles;
+  const int32_t* tile_count;
+  int32_t M;
+  // Epilogue operands.
+  void* C;                  // STORE: fp32 [rows, ldc]; SWIGLU: dtype [rows, ldc]
+  int64_t ldc;
+  float* C2;                // STORE: column N (if B2) -> C2[row]
+  const float* col_bias;    // STORE: + col_bias[n]
+  const float* row_scale;   // STORE: * row_scale[row]
+  float* acc_out;           // ATOMIC: [tokens, ldo]
+  int64_t ldo;
+  const int32_t* perm;      // ATOMIC: assignment id of each row (position)
+  const float* topk_w;      // ATOMIC: routing weight of each assignment id
+  int32_t topk;             // ATOMIC: K (token = assignment id / K)
+};
+
+// Tile configurations.  BM x BN output tile, 256 threads (4 waves as WM x WN).
+enum TileCfg : int {
+  TILE_SMALL = 0,  // BM=32,  BN=128 : decode-sized groups (weight streaming)
+  TILE_LARGE = 1,  // BM=128, BN=256 : prefill-sized groups
+};
+int tile_bm(TileCfg cfg);
+
+// dtype: 0 = fp32, 1 = bf16.  Returns hipSuccess or the launch error.
+hipError_t launch_gemm(int dtype, TileCfg cfg, Epilogue epi, const GemmParams& p, int64_t max_tiles,
+                       hipStream_t stream);
+
+// Router top-K: logits [T, E] fp32 -> idx/w [T, K]; optional gate logits [T] -> sigmoid.
+hipError_t launch_topk(const float* logits, int64_t T, int E, int K, int scoring, int renorm,
+                       int32_t* idx, float* w, const float* gate_logit, float* gate_out,
+                       hipStream_t stream);
+
+// Dispatch.
+int dispatch_segment_len(int64_t A);
+int64_t dispatch_num_segments(int64_t A);
+hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_counts,
+                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                           int bm, int32_t* tiles, int32_t* tile_count, hipStream_t stream);
+// Tile map from offsets alone (staged API).
+hipError_t launch_tile_map(const int32_t* offsets, int E, int bm, int32_t* tiles,
+                           int32_t* tile_count, hipStream_t stream);
+hipError_t launch_gather_rows(const void* x, int64_t D, int esize, const int32_t* perm,
+                              const int32_t* offsets, int E, int K, int64_t A, void* x_perm,
+                              hipStream_t stream);
+
+// Combine / finalize.
+hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
+                          const float* y_shared, const float* gate, int64_t T, int K, int D,
+                          void* out, int out_dtype, hipStream_t stream);
+hipError_t launch_cast(const float* src, void* dst, int64_t n, int out_dtype, hipStream_t stream);
+hipError_t launch_zero(float* dst, int64_t n, hipStream_t stream);
+
+}  // namespace moe

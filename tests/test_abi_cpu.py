@@ -1,0 +1,185 @@
+"""Host-side tests of the C ABI that need no GPU: the library loads, exports every function
+include/moe.h declares, the ctypes structs match the C layout, and invalid calls fail with
+the documented status before anything is launched.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from mixture_experts_layer_renorm_amd import abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return abi.load_library()
+
+
+def test_header_declares_the_five_stages_and_helpers():
+    names = _declared_functions()
+    for n in ("moe_route", "moe_dispatch", "moe_experts", "moe_combine", "moe_forward",
+              "moe_route_logits", "moe_workspace_size", "moe_status_string", "moe_last_error"):
+        assert n in names
+    assert set(names) == set(abi.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", abi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    assert set(_declared_functions()) <= exported
+
+
+def test_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(moe_problem),"
+        " offsetof(moe_problem, flags), offsetof(moe_problem, out_dtype), sizeof(moe_weights),"
+        " sizeof(moe_routing), offsetof(moe_routing, shared_gate));return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [ctypes.sizeof(abi.moe_problem), abi.moe_problem.flags.offset,
+            abi.moe_problem.out_dtype.offset, ctypes.sizeof(abi.moe_weights),
+            ctypes.sizeof(abi.moe_routing), abi.moe_routing.shared_gate.offset]
+    assert got == want
+
+
+def _prob(**kw):
+    base = dict(T=64, D=256, E=8, K=2, F=128)
+    base.update(kw)
+    import torch
+    return abi.make_problem(**base, dtype=torch.float32)
+
+
+def _ws_size(lib, p):
+    n = ctypes.c_size_t(0)
+    st = lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_and_validation(lib):
+    st, n = _ws_size(lib, _prob())
+    assert st == abi.MOE_OK and n > 0
+    assert _ws_size(lib, _prob(K=9))[0] == abi.MOE_ERR_INVALID_ARG      # K > E
+    assert _ws_size(lib, _prob(K=0))[0] == abi.MOE_ERR_INVALID_ARG      # K < 1
+    assert _ws_size(lib, _prob(T=-1))[0] == abi.MOE_ERR_INVALID_ARG
+    assert _ws_size(lib, _prob(D=100))[0] == abi.MOE_ERR_UNSUPPORTED    # D % 64
+    assert _ws_size(lib, _prob(F=96))[0] == abi.MOE_ERR_UNSUPPORTED
+    assert _ws_size(lib, _prob(E=2000, K=4))[0] == abi.MOE_ERR_UNSUPPORTED
+    assert _ws_size(lib, _prob(E=128, K=65))[0] == abi.MOE_ERR_UNSUPPORTED
+    p = _prob()
+    p.scoring = 7
+    assert _ws_size(lib, p)[0] == abi.MOE_ERR_INVALID_ARG
+    p = _prob()
+    p.flags = 0x80
+    assert _ws_size(lib, p)[0] == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_workspace_size(None, None) == abi.MOE_ERR_INVALID_ARG
+    assert b"NULL" in lib.moe_last_error()
+    # the workspace grows with T and with the deterministic flag
+    assert _ws_size(lib, _prob(T=128))[1] > _ws_size(lib, _prob(T=64))[1]
+    pd = _prob()
+    pd.flags = abi.MOE_FLAG_DETERMINISTIC
+    assert _ws_size(lib, pd)[1] > _ws_size(lib, _prob())[1]
+
+
+def test_status_strings(lib):
+    for code, name in [(0, b"MOE_OK"), (-1, b"MOE_ERR_INVALID_ARG"), (-2, b"MOE_ERR_UNSUPPORTED"),
+                       (-3, b"MOE_ERR_WORKSPACE"), (-4, b"MOE_ERR_HIP")]:
+        assert lib.moe_status_string(code) == name
+
+
+# Fake device addresses: never dereferenced, because validation rejects the call first.
+ALIGNED = 0x7F0000000000
+MISALIGNED = ALIGNED + 4
+
+
+def _weights(**kw):
+    w = abi.moe_weights()
+    for n in ("w_router", "w_gate_up", "w_down"):
+        setattr(w, n, ALIGNED)
+    for k, v in kw.items():
+        setattr(w, k, v)
+    return w
+
+
+def test_invalid_calls_fail_before_launch(lib):
+    p = _prob()
+    st, need = _ws_size(lib, p)
+    w = _weights()
+    r = abi.moe_routing()
+    out = ALIGNED
+    # NULL x / out
+    assert lib.moe_forward(ctypes.byref(p), None, ctypes.byref(w), None, out, ALIGNED, need,
+                           None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward(ctypes.byref(p), ALIGNED + 4096, ctypes.byref(w), None, None, ALIGNED,
+                           need, None) == abi.MOE_ERR_INVALID_ARG
+    # misaligned weight
+    wm = _weights(w_down=MISALIGNED)
+    assert lib.moe_forward(ctypes.byref(p), ALIGNED + 4096, ctypes.byref(wm), None, out, ALIGNED,
+                           need, None) == abi.MOE_ERR_INVALID_ARG
+    assert b"w_down" in lib.moe_last_error()
+    # workspace too small / missing
+    assert lib.moe_forward(ctypes.byref(p), ALIGNED + 4096, ctypes.byref(w), None, out, ALIGNED,
+                           need - 1, None) == abi.MOE_ERR_WORKSPACE
+    assert lib.moe_forward(ctypes.byref(p), ALIGNED + 4096, ctypes.byref(w), None, out, None,
+                           need, None) == abi.MOE_ERR_WORKSPACE
+    # out aliasing x
+    assert lib.moe_forward(ctypes.byref(p), out, ctypes.byref(w), None, out, ALIGNED, need,
+                           None) == abi.MOE_ERR_INVALID_ARG
+    # shared expert declared but its weights missing
+    ps = _prob(F_shared=64)
+    ps.shared_gated = 1
+    _, need_s = _ws_size(lib, ps)
+    assert lib.moe_forward(ctypes.byref(ps), ALIGNED + 4096, ctypes.byref(w), None, out, ALIGNED,
+                           need_s, None) == abi.MOE_ERR_INVALID_ARG
+    # route: required outputs missing; K > E
+    assert lib.moe_route(ctypes.byref(p), ALIGNED, ctypes.byref(w), ctypes.byref(r), ALIGNED,
+                         need, None) == abi.MOE_ERR_INVALID_ARG
+    pk = _prob(K=9)
+    r2 = abi.moe_routing(topk_idx=ALIGNED, topk_w=ALIGNED)
+    assert lib.moe_route_logits(ctypes.byref(pk), ALIGNED, ctypes.byref(r2),
+                                None) == abi.MOE_ERR_INVALID_ARG
+    # dispatch / experts / combine: missing routing tensors
+    assert lib.moe_dispatch(ctypes.byref(p), None, ctypes.byref(r), None, ALIGNED, need,
+                            None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_experts(ctypes.byref(p), ALIGNED, None, ctypes.byref(w), ctypes.byref(r),
+                           ALIGNED, None, ALIGNED, need, None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctypes.byref(p), ALIGNED, ctypes.byref(r), None, ALIGNED,
+                           None) == abi.MOE_ERR_INVALID_ARG
+
+
+def test_empty_batch_returns_ok_without_touching_pointers(lib):
+    p = _prob(T=0)
+    w = abi.moe_weights()
+    assert lib.moe_forward(ctypes.byref(p), None, ctypes.byref(w), None, None, None, 0,
+                           None) == abi.MOE_OK
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None, 0, None) == abi.MOE_OK
+    assert lib.moe_combine(ctypes.byref(p), None, None, None, None, None) == abi.MOE_OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    p = _prob()
+    with pytest.raises(ValueError):
+        abi._ptr(torch.zeros(4), "x")
+    with pytest.raises(RuntimeError):
+        abi.load_library(os.path.join(tempfile.gettempdir(), "does-not-exist", "libmoe.so"))

@@ -1,0 +1,149 @@
+"""End-to-end GPU parity of the layer (moe_forward and the staged API) against the CPU oracle.
+
+Sizes are chosen so the float64 oracle finishes in seconds while the GPU path still spans
+several tiles of both tile shapes and ragged tails.  Routing is compared bit-exactly on the
+GPU's exported fp32 logits, and the oracle computes the expert outputs from those same logits
+(the near-tie protocol: logits themselves are checked against the oracle's in
+test_gpu_route.py).  Outputs: max |err| <= 2e-2·RMS (bf16 layers) or 1e-4·RMS (fp32 layers)
+on the fp32 result; a bf16 output is additionally allowed its own rounding (half a bf16 ulp),
+and in deterministic mode must equal the round-to-nearest-even of the fp32 result bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_renorm_amd import abi
+from mixture_experts_layer_renorm_amd.synth import CONFIGS, hot_experts, make_layer
+from oracle import moe_oracle as O
+from tests.moe_testlib import (TOL_BF16, TOL_F32, TOL_ROUTING_W, bf16_half_ulp, f64, i64,
+                               oracle_args, problem_for, rel_max_err, weights_for)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+CASES = {
+    # name: (workload, overrides, T)
+    "tiny": ("tiny", {}, 64),
+    "tiny_large_tiles": ("tiny", {}, 1000),
+    "a3b_decode": ("a3b_decode", {}, 64),
+    "a3b_E16": ("a3b_prefill", {"E": 16}, 600),
+    "a3b_T1": ("a3b_prefill", {}, 1),
+    "a17b_E32": ("a17b", {"E": 32}, 400),
+    "ds_sigmoid_E16": ("ds_sigmoid", {"E": 16}, 333),
+    "skew_E64": ("skew", {"E": 64, "hot_stride": 8}, 500),
+    "skew_conc_E64": ("skew_conc", {"E": 64, "hot_stride": 8}, 300),
+}
+
+
+def _case(name):
+    wl, over, T = CASES[name]
+    cfg = CONFIGS[wl].with_(**over)
+    layer = make_layer(cfg, device=DEV, T=T)
+    return cfg, layer, T
+
+
+def _forward(cfg, layer, T, out_dtype, deterministic):
+    p = problem_for(cfg, T=T, out_dtype=out_dtype, deterministic=deterministic)
+    r = abi.alloc_routing(p, DEV)
+    out = torch.empty((T, cfg.D), dtype=out_dtype, device=DEV)
+    abi.moe_forward(p, layer["x"], weights_for(layer), r, out, abi.alloc_workspace(p, DEV))
+    torch.cuda.synchronize()
+    return out, r
+
+
+def _oracle(cfg, layer, logits):
+    args, kw = oracle_args(cfg, layer)
+    return O.moe_forward(*args, logits=f64(logits), **kw)
+
+
+def _check_routing(cfg, r, ref):
+    np.testing.assert_array_equal(i64(r["topk_idx"]), ref["topk_idx"])
+    np.testing.assert_allclose(f64(r["topk_w"]), ref["topk_w"], rtol=0, atol=TOL_ROUTING_W)
+    n = int(ref["offsets"][cfg.E])
+    np.testing.assert_array_equal(i64(r["expert_counts"]), ref["counts"])
+    np.testing.assert_array_equal(i64(r["expert_offsets"]), ref["offsets"])
+    np.testing.assert_array_equal(i64(r["perm"])[:n], ref["perm"])
+    np.testing.assert_array_equal(i64(r["inv_perm"]), ref["inv_perm"])
+
+
+def _tol(cfg):
+    return TOL_F32 if cfg.dtype == "f32" else TOL_BF16
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("deterministic", [True, False])
+def test_forward_matches_oracle(name, deterministic):
+    cfg, layer, T = _case(name)
+    out32, r = _forward(cfg, layer, T, torch.float32, deterministic)
+    ref = _oracle(cfg, layer, r["logits"])
+    _check_routing(cfg, r, ref)
+    if cfg.shared_gated:
+        np.testing.assert_allclose(f64(r["shared_gate"][:T]), ref["gate"], rtol=0, atol=1e-5)
+    err = rel_max_err(out32, ref["out"])
+    assert err <= _tol(cfg), f"{name}: max|err|/RMS = {err:.3e}"
+    if cfg.dtype == "bf16":
+        outb, rb = _forward(cfg, layer, T, torch.bfloat16, deterministic)
+        assert torch.equal(rb["topk_idx"], r["topk_idx"])
+        if deterministic:
+            assert torch.equal(outb, out32.to(torch.bfloat16))
+        got = f64(outb)
+        rms = float(np.sqrt(np.mean(ref["out"] ** 2)))
+        bound = _tol(cfg) * rms + bf16_half_ulp(ref["out"])
+        assert np.all(np.abs(got - ref["out"]) <= bound)
+
+
+@pytest.mark.parametrize("name", ["tiny", "a3b_E16", "a17b_E32", "ds_sigmoid_E16", "a3b_decode"])
+def test_staged_api_matches_oracle(name):
+    cfg, layer, T = _case(name)
+    p = problem_for(cfg, T=T, out_dtype=torch.float32)
+    ws = abi.alloc_workspace(p, DEV)
+    r = abi.alloc_routing(p, DEV)
+    w = weights_for(layer)
+    x = layer["x"]
+    abi.moe_route(p, x, w, r, ws)
+    x_perm = torch.empty((T * cfg.K, cfg.D), dtype=cfg.torch_dtype, device=DEV)
+    abi.moe_dispatch(p, x, r, x_perm, ws)
+    A = T * cfg.K
+    y_perm = torch.empty((A, cfg.D), dtype=torch.float32, device=DEV)
+    y_perm2 = torch.empty((A, cfg.D), dtype=torch.float32, device=DEV)
+    y_shared = (torch.empty((T, cfg.D), dtype=torch.float32, device=DEV)
+                if cfg.F_shared else None)
+    abi.moe_experts(p, x, None, w, r, y_perm, y_shared, ws)       # rows gathered on load
+    abi.moe_experts(p, None, x_perm, w, r, y_perm2, None, ws)     # rows from x_perm
+    out = torch.empty((T, cfg.D), dtype=torch.float32, device=DEV)
+    abi.moe_combine(p, y_perm, r, y_shared, out)
+    torch.cuda.synchronize()
+    ref = _oracle(cfg, layer, r["logits"])
+    _check_routing(cfg, r, ref)
+    assert torch.equal(y_perm, y_perm2)
+    tol = _tol(cfg)
+    assert rel_max_err(y_perm, ref["y_perm"]) <= tol
+    if cfg.F_shared:
+        assert rel_max_err(y_shared, ref["y_shared"]) <= tol
+    assert rel_max_err(out, ref["out"]) <= tol
+
+
+def test_deterministic_forward_is_bitwise_reproducible():
+    cfg, layer, T = _case("a17b_E32")
+    a, _ = _forward(cfg, layer, T, torch.bfloat16, True)
+    b, _ = _forward(cfg, layer, T, torch.bfloat16, True)
+    assert torch.equal(a, b)
+
+
+def test_empty_batch_is_noop():
+    cfg = CONFIGS["tiny"]
+    p = problem_for(cfg, T=0)
+    out = torch.full((1, cfg.D), 7.0, device=DEV)
+    layer = make_layer(cfg, device=DEV, T=1)
+    abi.moe_forward(p, layer["x"], weights_for(layer), None, out, abi.alloc_workspace(p, DEV))
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+def test_concentrated_routing_hits_eight_experts():
+    cfg, layer, T = _case("skew_conc_E64")
+    _, r = _forward(cfg, layer, T, torch.float32, False)
+    counts = i64(r["expert_counts"])
+    assert sorted(np.nonzero(counts)[0].tolist()) == hot_experts(cfg)
+    assert np.all(counts[hot_experts(cfg)] == T)
