@@ -55,14 +55,20 @@ typedef enum {
 } moe_scoring;
 
 enum {
-  MOE_FLAG_DETERMINISTIC = 1u, /* combine by gathering each token's K rows in slot order
-                                  (bitwise reproducible); default: fused fp32 atomics      */
+  MOE_FLAG_ATOMIC_COMBINE = 1u, /* fuse the combine into the down GEMM with fp32 atomic
+                                   adds into a [T,D] accumulator: no [T*K,D] buffer, but the
+                                   summation order (and so the last bits) varies run to run.
+                                   Default: each expert row is stored and a gather kernel sums
+                                   each token's K rows in slot order (bitwise reproducible;
+                                   measured faster on MI355X, whose device-scope float
+                                   atomics do not resolve in the per-XCD L2)              */
   MOE_FLAG_NO_RENORM = 2u      /* a = p_e without renormalisation over I_t (the plain
                                   top-k sum of "Qwen3.8-Flash-Next 架构笔记 · 04" §2)       */
 };
 
 /* Problem statement (host struct, read during the call, not retained).
- * v1 limits: D, F and F_shared multiples of 64; 1 <= E <= 1024; 1 <= K <= E; T*K < 2^31. */
+ * v1 limits: D, F and F_shared multiples of 64; 1 <= E <= 1024; 1 <= K <= min(E, 64);
+ * T*K < 2^31. */
 typedef struct {
   int64_t T;            /* tokens (batch x sequence flattened)                             */
   int32_t D;            /* hidden width                                                    */
@@ -115,7 +121,7 @@ int moe_workspace_size(const moe_problem *p, size_t *bytes);
  * Out: r->topk_idx, r->topk_w (required); r->logits (optional, [T,E] fp32);
  *      r->shared_gate (optional, only written for a gated shared expert).
  * Logits are fp32 MFMA accumulations of the dtype inputs; selection compares these fp32
- * values exactly (NaN ranks below -inf's equal, -0 == +0). */
+ * values exactly (a NaN logit ranks as -inf; -0 equals +0). */
 int moe_route(const moe_problem *p, const void *x, const moe_weights *w, moe_routing *r,
               void *workspace, size_t workspace_bytes, moe_stream_t stream);
 
@@ -152,10 +158,30 @@ int moe_combine(const moe_problem *p, const float *y_perm, const moe_routing *r,
 /* The whole layer: router, dispatch, grouped gate_up GEMM with fused SiLU*up, grouped down
  * GEMM with fused weighted combine, shared expert, final cast.  out: [T, D] out_dtype.
  * r_opt may be NULL; each non-NULL field of *r_opt receives the corresponding intermediate.
- * Without MOE_FLAG_DETERMINISTIC the combine uses fp32 atomics (run-to-run bit differences
- * within fp32 rounding); with it, the staged gather combine is used. */
+ * By default the combine gathers each token's K expert rows in slot order (bitwise
+ * reproducible); MOE_FLAG_ATOMIC_COMBINE selects the fused atomic epilogue instead. */
 int moe_forward(const moe_problem *p, const void *x, const moe_weights *w, moe_routing *r_opt,
                 void *out, void *workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* Stage boundaries recorded by moe_forward_timed, in launch order. */
+enum {
+  MOE_STAGE_ROUTER = 0,   /* router GEMM (+ shared-gate column)                        */
+  MOE_STAGE_TOPK = 1,     /* top-K selection and weights                               */
+  MOE_STAGE_DISPATCH = 2, /* histogram, scan + tile map, stable scatter                */
+  MOE_STAGE_GATE_UP = 3,  /* routed grouped gate_up GEMM with fused SiLU*up            */
+  MOE_STAGE_SHARED = 4,   /* shared expert (atomic mode: or the accumulator zero-fill) */
+  MOE_STAGE_DOWN = 5,     /* routed grouped down GEMM (+ fused combine in atomic mode)  */
+  MOE_STAGE_FINAL = 6,    /* gather combine (default), or the final cast (atomic mode) */
+  MOE_STAGE_COUNT = 7
+};
+
+/* moe_forward with timing: events[i] (a caller-created hipEvent_t, passed as void*) is
+ * recorded on `stream` right before stage i is launched and events[MOE_STAGE_COUNT] after
+ * the last one, so hipEventElapsedTime(events[i], events[i+1]) brackets stage i.  `events`
+ * must hold MOE_STAGE_COUNT + 1 valid events.  Same results and errors as moe_forward. */
+int moe_forward_timed(const moe_problem *p, const void *x, const moe_weights *w,
+                      moe_routing *r_opt, void *out, void *workspace, size_t workspace_bytes,
+                      moe_stream_t stream, void *const *events);
 
 /* Static text for a status code. */
 const char *moe_status_string(int status);

@@ -27,11 +27,14 @@ MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
 MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1
-MOE_FLAG_DETERMINISTIC = 1
+MOE_FLAG_ATOMIC_COMBINE = 1
 MOE_FLAG_NO_RENORM = 2
 
 SYMBOLS = ("moe_workspace_size", "moe_route", "moe_route_logits", "moe_dispatch",
-           "moe_experts", "moe_combine", "moe_forward", "moe_status_string", "moe_last_error")
+           "moe_experts", "moe_combine", "moe_forward", "moe_forward_timed",
+           "moe_status_string", "moe_last_error")
+MOE_STAGE_NAMES = ("router", "topk", "dispatch", "gate_up", "shared", "down", "final")
+MOE_STAGE_COUNT = len(MOE_STAGE_NAMES)
 
 _DTYPE_CODE = {torch.float32: MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16}
 _DTYPE_OF_CODE = {MOE_DTYPE_F32: torch.float32, MOE_DTYPE_BF16: torch.bfloat16}
@@ -86,8 +89,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_experts.argtypes = [prob, vp, vp, P(moe_weights), P(moe_routing), vp, vp, vp, sz, vp]
     lib.moe_combine.argtypes = [prob, vp, P(moe_routing), vp, vp, vp]
     lib.moe_forward.argtypes = [prob, vp, P(moe_weights), P(moe_routing), vp, vp, sz, vp]
+    lib.moe_forward_timed.argtypes = [prob, vp, P(moe_weights), P(moe_routing), vp, vp, sz, vp,
+                                      P(ctypes.c_void_p)]
     for n in ("moe_workspace_size", "moe_route", "moe_route_logits", "moe_dispatch",
-              "moe_experts", "moe_combine", "moe_forward"):
+              "moe_experts", "moe_combine", "moe_forward", "moe_forward_timed"):
         getattr(lib, n).restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -107,12 +112,12 @@ def _check(status: int) -> None:
 
 def make_problem(T: int, D: int, E: int, K: int, F: int, F_shared: int = 0,
                  shared_gated: bool = False, scoring: str = "softmax", dtype=torch.bfloat16,
-                 out_dtype=None, deterministic: bool = False,
+                 out_dtype=None, atomic_combine: bool = False,
                  renormalize: bool = True) -> moe_problem:
     if scoring not in ("softmax", "sigmoid"):
         raise ValueError(f"scoring must be 'softmax' or 'sigmoid', got {scoring!r}")
     out_dtype = dtype if out_dtype is None else out_dtype
-    flags = (MOE_FLAG_DETERMINISTIC if deterministic else 0) | \
+    flags = (MOE_FLAG_ATOMIC_COMBINE if atomic_combine else 0) | \
             (0 if renormalize else MOE_FLAG_NO_RENORM)
     return moe_problem(T=T, D=D, E=E, K=K, F=F, F_shared=F_shared,
                        shared_gated=1 if shared_gated else 0,
@@ -241,6 +246,21 @@ def moe_forward(p: moe_problem, x: torch.Tensor, weights: Dict, routing: Optiona
                            ctypes.byref(r) if r is not None else None,
                            _ptr(out, "out", _DTYPE_OF_CODE[p.out_dtype]), wp, wb,
                            _stream(stream)))
+
+
+def moe_forward_timed(p: moe_problem, x: torch.Tensor, weights: Dict, routing: Optional[Dict],
+                      out: torch.Tensor, workspace: torch.Tensor, events, stream=None) -> None:
+    """moe_forward recording `events` (MOE_STAGE_COUNT + 1 raw hipEvent_t handles as ints)."""
+    lib = load_library()
+    if len(events) != MOE_STAGE_COUNT + 1:
+        raise ValueError(f"need {MOE_STAGE_COUNT + 1} events")
+    w, r = _weights(p, weights), _routing(routing)
+    wp, wb = _ws(workspace)
+    ev = (ctypes.c_void_p * len(events))(*events)
+    _check(lib.moe_forward_timed(ctypes.byref(p), _ptr(x, "x", problem_dtype(p)), ctypes.byref(w),
+                                 ctypes.byref(r) if r is not None else None,
+                                 _ptr(out, "out", _DTYPE_OF_CODE[p.out_dtype]), wp, wb,
+                                 _stream(stream), ev))
 
 
 # ------------------------------------------------------------- allocation helpers ----

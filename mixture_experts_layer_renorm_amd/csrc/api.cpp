@@ -53,7 +53,7 @@ int check_problem(const moe_problem* p) {
     return fail(MOE_ERR_INVALID_ARG, "unknown out_dtype %d", p->out_dtype);
   if (p->shared_gated != 0 && p->shared_gated != 1)
     return fail(MOE_ERR_INVALID_ARG, "shared_gated must be 0 or 1");
-  if (p->flags & ~(uint32_t)(MOE_FLAG_DETERMINISTIC | MOE_FLAG_NO_RENORM))
+  if (p->flags & ~(uint32_t)(MOE_FLAG_ATOMIC_COMBINE | MOE_FLAG_NO_RENORM))
     return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
   if (p->D % 64 || p->F % 64 || p->F_shared % 64)
     return fail(MOE_ERR_UNSUPPORTED, "D, F and F_shared must be multiples of 64 (D=%d F=%d Fs=%d)",
@@ -108,12 +108,13 @@ Layout layout(const moe_problem* p) {
   L.tile_count = take(16);
   L.H = take((size_t)A * p->F * es);
   L.Hs = take((size_t)T * p->F_shared * es);
-  L.acc = take((size_t)T * D * 4);
-  if (p->flags & MOE_FLAG_DETERMINISTIC) {
+  if (p->flags & MOE_FLAG_ATOMIC_COMBINE) {
+    L.acc = take(p->out_dtype == MOE_DTYPE_F32 ? 0 : (size_t)T * D * 4);
+    L.y_perm = L.y_shared = 0;
+  } else {
+    L.acc = 0;
     L.y_perm = take((size_t)A * D * 4);
     L.y_shared = take(has_shared(p) ? (size_t)T * D * 4 : 0);
-  } else {
-    L.y_perm = L.y_shared = 0;
   }
   L.total = off;
   return L;
@@ -432,8 +433,13 @@ int moe_combine(const moe_problem* p, const float* y_perm, const moe_routing* r,
   return MOE_OK;
 }
 
-int moe_forward(const moe_problem* p, const void* x, const moe_weights* w, moe_routing* r_opt,
-                void* out, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_routing* r_opt,
+                 void* out, void* workspace, size_t workspace_bytes, moe_stream_t stream,
+                 void* const* events) {
   g_last_error.clear();
   int st = check_problem(p);
   if (st) return st;
@@ -470,10 +476,15 @@ int moe_forward(const moe_problem* p, const void* x, const moe_weights* w, moe_r
   const int64_t A = p->T * p->K;
   const bool g = gated(p);
   float* gate_logit = at<float>(ws, L.gate_logit);
+  auto mark = [&](int stage) -> hipError_t {
+    return events ? hipEventRecord((hipEvent_t)events[stage], s) : hipSuccess;
+  };
 
   // 1. router GEMM (+ shared-gate column) and top-K
+  MOE_HIP_TRY(mark(MOE_STAGE_ROUTER), "event record");
   MOE_HIP_TRY(run_router(p, x, w, r.logits, g ? gate_logit : nullptr, g ? w->ws_gate : nullptr, s),
               "router GEMM launch");
+  MOE_HIP_TRY(mark(MOE_STAGE_TOPK), "event record");
   MOE_HIP_TRY(moe::launch_topk(r.logits, p->T, p->E, p->K, p->scoring,
                                !(p->flags & MOE_FLAG_NO_RENORM), r.topk_idx, r.topk_w,
                                g ? gate_logit : nullptr, g ? r.shared_gate : nullptr, s),
@@ -483,43 +494,78 @@ int moe_forward(const moe_problem* p, const void* x, const moe_weights* w, moe_r
   const int bm = moe::tile_bm(cfg);
   int32_t* tiles = at<int32_t>(ws, L.tiles);
   int32_t* tile_count = at<int32_t>(ws, L.tile_count);
+  MOE_HIP_TRY(mark(MOE_STAGE_DISPATCH), "event record");
   MOE_HIP_TRY(moe::launch_dispatch(r.topk_idx, A, p->E, at<int32_t>(ws, L.seg_counts),
                                    r.expert_counts, r.expert_offsets, r.perm, r.inv_perm, bm, tiles,
                                    tile_count, s),
               "dispatch launch");
   // 3. routed gate_up with SiLU*up
   void* H = at<void>(ws, L.H);
+  MOE_HIP_TRY(mark(MOE_STAGE_GATE_UP), "event record");
   MOE_HIP_TRY(run_gate_up(p, x, nullptr, w->w_gate_up, r.perm, tiles, tile_count, L.max_mtiles, H,
                           cfg, s),
               "gate_up GEMM launch");
   const float* gate = g ? r.shared_gate : nullptr;
-  if (p->flags & MOE_FLAG_DETERMINISTIC) {
+  if (!(p->flags & MOE_FLAG_ATOMIC_COMBINE)) {
+    // 4. shared expert and routed down into fp32 buffers, then the gather combine
     float* y_perm = at<float>(ws, L.y_perm);
     float* y_shared = has_shared(p) ? at<float>(ws, L.y_shared) : nullptr;
-    MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, cfg, y_perm, nullptr,
-                         nullptr, nullptr, s),
-                "down GEMM launch");
+    MOE_HIP_TRY(mark(MOE_STAGE_SHARED), "event record");
     if (y_shared)
       MOE_HIP_TRY(run_shared(p, x, w, at<void>(ws, L.Hs), y_shared, nullptr, s),
                   "shared expert launch");
+    MOE_HIP_TRY(mark(MOE_STAGE_DOWN), "event record");
+    MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, cfg, y_perm, nullptr,
+                         nullptr, nullptr, s),
+                "down GEMM launch");
+    MOE_HIP_TRY(mark(MOE_STAGE_FINAL), "event record");
     MOE_HIP_TRY(moe::launch_combine(y_perm, r.inv_perm, r.topk_w, y_shared, gate, p->T, p->K,
                                     p->D, out, p->out_dtype, s),
                 "combine launch");
+    MOE_HIP_TRY(mark(MOE_STAGE_COUNT), "event record");
     return MOE_OK;
   }
-  // 4. fp32 accumulator: the shared branch initialises it (or it is zeroed), then the down
-  //    GEMM adds the weighted routed rows with atomics, then one cast to the output dtype.
+  // 4'. atomic mode: the shared branch initialises an fp32 accumulator (or it is zeroed), the
+  //     down GEMM adds the weighted routed rows with atomics, then one cast to the output dtype.
   float* acc = p->out_dtype == MOE_DTYPE_F32 ? static_cast<float*>(out) : at<float>(ws, L.acc);
+  MOE_HIP_TRY(mark(MOE_STAGE_SHARED), "event record");
   if (has_shared(p))
     MOE_HIP_TRY(run_shared(p, x, w, at<void>(ws, L.Hs), acc, gate, s), "shared expert launch");
   else
     MOE_HIP_TRY(moe::launch_zero(acc, p->T * p->D, s), "zero launch");
+  MOE_HIP_TRY(mark(MOE_STAGE_DOWN), "event record");
   MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, cfg, nullptr, acc, r.perm,
                        r.topk_w, s),
               "down GEMM launch");
+  MOE_HIP_TRY(mark(MOE_STAGE_FINAL), "event record");
   if (p->out_dtype != MOE_DTYPE_F32)
     MOE_HIP_TRY(moe::launch_cast(acc, out, p->T * p->D, p->out_dtype, s), "cast launch");
+  MOE_HIP_TRY(mark(MOE_STAGE_COUNT), "event record");
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const moe_problem* p, const void* x, const moe_weights* w, moe_routing* r_opt,
+                void* out, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  return forward_impl(p, x, w, r_opt, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_forward_timed(const moe_problem* p, const void* x, const moe_weights* w,
+                      moe_routing* r_opt, void* out, void* workspace, size_t workspace_bytes,
+                      moe_stream_t stream, void* const* events) {
+  if (!events) {
+    g_last_error.clear();
+    return fail(MOE_ERR_INVALID_ARG, "events is NULL");
+  }
+  for (int i = 0; i <= MOE_STAGE_COUNT; ++i)
+    if (!events[i]) {
+      g_last_error.clear();
+      return fail(MOE_ERR_INVALID_ARG, "events[%d] is NULL", i);
+    }
+  return forward_impl(p, x, w, r_opt, out, workspace, workspace_bytes, stream, events);
 }
 
 }  // extern "C"

@@ -43,14 +43,14 @@ class LazyRows:
         return self.t.shape[0]
 
 
-def problem_for(cfg: LayerConfig, T=None, out_dtype=None, deterministic=False,
+def problem_for(cfg: LayerConfig, T=None, out_dtype=None, atomic_combine=False,
                 renormalize=True):
     dt = cfg.torch_dtype
     return abi.make_problem(T=cfg.T if T is None else T, D=cfg.D, E=cfg.E, K=cfg.K, F=cfg.F,
                             F_shared=cfg.F_shared, shared_gated=cfg.shared_gated,
                             scoring=cfg.scoring, dtype=dt,
                             out_dtype=dt if out_dtype is None else out_dtype,
-                            deterministic=deterministic, renormalize=renormalize)
+                            atomic_combine=atomic_combine, renormalize=renormalize)
 
 
 def weights_for(layer) -> dict:

@@ -94,11 +94,11 @@ def test_workspace_size_and_validation(lib):
     assert _ws_size(lib, p)[0] == abi.MOE_ERR_INVALID_ARG
     assert lib.moe_workspace_size(None, None) == abi.MOE_ERR_INVALID_ARG
     assert b"NULL" in lib.moe_last_error()
-    # the workspace grows with T and with the deterministic flag
+    # the workspace grows with T; the atomic combine needs no [T*K, D] row buffer
     assert _ws_size(lib, _prob(T=128))[1] > _ws_size(lib, _prob(T=64))[1]
-    pd = _prob()
-    pd.flags = abi.MOE_FLAG_DETERMINISTIC
-    assert _ws_size(lib, pd)[1] > _ws_size(lib, _prob())[1]
+    pa = _prob()
+    pa.flags = abi.MOE_FLAG_ATOMIC_COMBINE
+    assert _ws_size(lib, pa)[1] < _ws_size(lib, _prob())[1]
 
 
 def test_status_strings(lib):

@@ -6,7 +6,8 @@ GPU's exported fp32 logits, and the oracle computes the expert outputs from thos
 (the near-tie protocol: logits themselves are checked against the oracle's in
 test_gpu_route.py).  Outputs: max |err| <= 2e-2·RMS (bf16 layers) or 1e-4·RMS (fp32 layers)
 on the fp32 result; a bf16 output is additionally allowed its own rounding (half a bf16 ulp),
-and in deterministic mode must equal the round-to-nearest-even of the fp32 result bit for bit.
+and with the (default) gather combine must equal the round-to-nearest-even of the fp32 result
+bit for bit.
 """
 
 import numpy as np
@@ -43,8 +44,8 @@ def _case(name):
     return cfg, layer, T
 
 
-def _forward(cfg, layer, T, out_dtype, deterministic):
-    p = problem_for(cfg, T=T, out_dtype=out_dtype, deterministic=deterministic)
+def _forward(cfg, layer, T, out_dtype, atomic):
+    p = problem_for(cfg, T=T, out_dtype=out_dtype, atomic_combine=atomic)
     r = abi.alloc_routing(p, DEV)
     out = torch.empty((T, cfg.D), dtype=out_dtype, device=DEV)
     abi.moe_forward(p, layer["x"], weights_for(layer), r, out, abi.alloc_workspace(p, DEV))
@@ -72,10 +73,10 @@ def _tol(cfg):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("deterministic", [True, False])
-def test_forward_matches_oracle(name, deterministic):
+@pytest.mark.parametrize("atomic", [False, True])
+def test_forward_matches_oracle(name, atomic):
     cfg, layer, T = _case(name)
-    out32, r = _forward(cfg, layer, T, torch.float32, deterministic)
+    out32, r = _forward(cfg, layer, T, torch.float32, atomic)
     ref = _oracle(cfg, layer, r["logits"])
     _check_routing(cfg, r, ref)
     if cfg.shared_gated:
@@ -83,9 +84,9 @@ def test_forward_matches_oracle(name, deterministic):
     err = rel_max_err(out32, ref["out"])
     assert err <= _tol(cfg), f"{name}: max|err|/RMS = {err:.3e}"
     if cfg.dtype == "bf16":
-        outb, rb = _forward(cfg, layer, T, torch.bfloat16, deterministic)
+        outb, rb = _forward(cfg, layer, T, torch.bfloat16, atomic)
         assert torch.equal(rb["topk_idx"], r["topk_idx"])
-        if deterministic:
+        if not atomic:
             assert torch.equal(outb, out32.to(torch.bfloat16))
         got = f64(outb)
         rms = float(np.sqrt(np.mean(ref["out"] ** 2)))
@@ -126,8 +127,8 @@ def test_staged_api_matches_oracle(name):
 
 def test_deterministic_forward_is_bitwise_reproducible():
     cfg, layer, T = _case("a17b_E32")
-    a, _ = _forward(cfg, layer, T, torch.bfloat16, True)
-    b, _ = _forward(cfg, layer, T, torch.bfloat16, True)
+    a, _ = _forward(cfg, layer, T, torch.bfloat16, False)
+    b, _ = _forward(cfg, layer, T, torch.bfloat16, False)
     assert torch.equal(a, b)
 
 
@@ -143,7 +144,7 @@ def test_empty_batch_is_noop():
 
 def test_concentrated_routing_hits_eight_experts():
     cfg, layer, T = _case("skew_conc_E64")
-    _, r = _forward(cfg, layer, T, torch.float32, False)
+    _, r = _forward(cfg, layer, T, torch.float32, True)
     counts = i64(r["expert_counts"])
     assert sorted(np.nonzero(counts)[0].tolist()) == hot_experts(cfg)
     assert np.all(counts[hot_experts(cfg)] == T)
