@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -68,11 +69,36 @@ int check_problem(const moe_problem* p) {
 bool has_shared(const moe_problem* p) { return p->F_shared > 0; }
 bool gated(const moe_problem* p) { return p->F_shared > 0 && p->shared_gated; }
 
+// Grouped (routed-expert) GEMMs.  The host does not see the per-expert counts (no sync), so the
+// tile is chosen from the mean rows per expert A/E.  bf16 groups of up to ~170 rows are bound by
+// weight reads and take the weight-streaming GEMM with an M tile that holds a whole typical
+// expert; larger groups (and fp32) take the LDS tile GEMM.  MOE_GROUPED_TILE (small, large,
+// stream64, stream128, stream192) overrides the choice, for tuning and for tests that cover
+// every tile shape at small sizes; the streaming shapes apply to bf16 only.
 moe::TileCfg grouped_cfg(const moe_problem* p) {
+  if (const char* o = std::getenv("MOE_GROUPED_TILE")) {
+    const bool bf = p->dtype == MOE_DTYPE_BF16;
+    if (!std::strcmp(o, "small")) return moe::TILE_SMALL;
+    if (!std::strcmp(o, "large")) return moe::TILE_LARGE;
+    if (bf && !std::strcmp(o, "stream64")) return moe::TILE_STREAM_64;
+    if (bf && !std::strcmp(o, "stream128")) return moe::TILE_STREAM_128;
+    if (bf && !std::strcmp(o, "stream192")) return moe::TILE_STREAM_192;
+  }
   const int64_t A = p->T * p->K;
-  return A <= (int64_t)48 * p->E ? moe::TILE_SMALL : moe::TILE_LARGE;
+  const double mean = (double)A / p->E;
+  if (p->dtype == MOE_DTYPE_BF16) {
+    if (mean <= 24) return moe::TILE_STREAM_64;
+    if (mean <= 170) return moe::TILE_STREAM_192;
+    return moe::TILE_LARGE;
+  }
+  return mean <= 48 ? moe::TILE_SMALL : moe::TILE_LARGE;
 }
-moe::TileCfg dense_cfg(int64_t M) { return M <= 256 ? moe::TILE_SMALL : moe::TILE_LARGE; }
+// Dense GEMMs (router, shared expert): large tiles unless they would leave CUs idle.
+moe::TileCfg dense_cfg(int64_t M, int64_t N) {
+  const int64_t bm = moe::tile_bm(moe::TILE_LARGE), bn = moe::tile_bn(moe::TILE_LARGE);
+  return ((M + bm - 1) / bm) * ((N + bn - 1) / bn) >= moe::kCus ? moe::TILE_LARGE
+                                                                  : moe::TILE_SMALL;
+}
 
 // Workspace layout: every region 256-byte aligned.
 struct Layout {
@@ -163,7 +189,7 @@ hipError_t run_router(const moe_problem* p, const void* x, const moe_weights* w,
   g.ldc = p->E;
   g.C2 = gate_logit;
   g.col_bias = w->logit_bias;
-  const moe::TileCfg cfg = dense_cfg(p->T);
+  const moe::TileCfg cfg = dense_cfg(p->T, p->E + (gate_w ? 1 : 0));
   const int bm = moe::tile_bm(cfg);
   return moe::launch_gemm(p->dtype, cfg, moe::EPI_STORE, g, (p->T + bm - 1) / bm, s);
 }
@@ -222,7 +248,7 @@ hipError_t run_down(const moe_problem* p, const void* H, const void* w_d, const 
 hipError_t run_shared(const moe_problem* p, const void* x, const moe_weights* w, void* Hs,
                       float* out, const float* row_scale, hipStream_t s) {
   const size_t es = esize(p->dtype);
-  const moe::TileCfg cfg = dense_cfg(p->T);
+  const moe::TileCfg cfg = dense_cfg(p->T, (int64_t)2 * p->F_shared);
   const int bm = moe::tile_bm(cfg);
   const int64_t mt = (p->T + bm - 1) / bm;
   moe::GemmParams g{};

@@ -339,19 +339,32 @@ hipError_t launch_cfg(Epilogue epi, const GemmParams& p, int64_t max_mtiles, int
 
 }  // namespace
 
-int tile_bm(TileCfg cfg) { return cfg == TILE_SMALL ? 32 : 128; }
+int tile_bm(TileCfg cfg) {
+  switch (cfg) {
+    case TILE_SMALL: return 32;
+    case TILE_LARGE: return 256;
+    case TILE_STREAM_64: return 64;
+    case TILE_STREAM_192: return 192;
+    case TILE_STREAM_128: return 128;
+  }
+  return 256;
+}
+int tile_bn(TileCfg) { return 128; }
 
 hipError_t launch_gemm(int dtype, TileCfg cfg, Epilogue epi, const GemmParams& p,
                        int64_t max_mtiles, hipStream_t stream) {
   if (max_mtiles <= 0) return hipSuccess;
+  if (cfg >= TILE_STREAM_64) return launch_stream_gemm(cfg, epi, p, max_mtiles, stream);
   // Occupancy from LDS: SMALL stages 4 x 20 KiB (2 work-groups per CU), LARGE 3 x 48 KiB (1).
+  // LARGE is 256 rows x 128 columns: one M tile holds every row of an expert with up to 256
+  // tokens, so that expert's weights stream from HBM once.
   if (dtype == 1) {
     if (cfg == TILE_SMALL)
       return launch_cfg<__bf16, 32, 128, 1, 4, 4>(epi, p, max_mtiles, 2, stream);
-    return launch_cfg<__bf16, 128, 256, 2, 2, 3>(epi, p, max_mtiles, 1, stream);
+    return launch_cfg<__bf16, 256, 128, 4, 1, 3>(epi, p, max_mtiles, 1, stream);
   }
   if (cfg == TILE_SMALL) return launch_cfg<float, 32, 128, 1, 4, 4>(epi, p, max_mtiles, 2, stream);
-  return launch_cfg<float, 128, 256, 2, 2, 3>(epi, p, max_mtiles, 1, stream);
+  return launch_cfg<float, 256, 128, 4, 1, 3>(epi, p, max_mtiles, 1, stream);
 }
 
 }  // namespace moe

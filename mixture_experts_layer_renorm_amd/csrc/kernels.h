@@ -51,10 +51,18 @@ struct GemmParams {
 
 // Tile configurations.  BM x BN output tile, 256 threads (4 waves as WM x WN).
 enum TileCfg : int {
-  TILE_SMALL = 0,  // BM=32,  BN=128 : decode-sized groups (weight streaming)
-  TILE_LARGE = 1,  // BM=128, BN=256 : prefill-sized groups
+  TILE_SMALL = 0,       // tile GEMM, BM=32,  BN=128
+  TILE_LARGE = 1,       // tile GEMM, BM=256, BN=128
+  TILE_STREAM_64 = 2,   // weight-streaming GEMM, BM=64 (decode-sized groups), bf16 only
+  TILE_STREAM_192 = 3,  // weight-streaming GEMM, BM=192, bf16 only
+  TILE_STREAM_128 = 4,  // weight-streaming GEMM, BM=128, bf16 only
 };
 int tile_bm(TileCfg cfg);
+int tile_bn(TileCfg cfg);
+
+// Grouped weight-streaming GEMM (tile map required, no B2 column), bf16.
+hipError_t launch_stream_gemm(TileCfg cfg, Epilogue epi, const GemmParams& p, int64_t max_mtiles,
+                              hipStream_t stream);
 
 // dtype: 0 = fp32, 1 = bf16.  Returns hipSuccess or the launch error.
 hipError_t launch_gemm(int dtype, TileCfg cfg, Epilogue epi, const GemmParams& p, int64_t max_tiles,

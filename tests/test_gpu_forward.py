@@ -34,6 +34,9 @@ CASES = {
     "ds_sigmoid_E16": ("ds_sigmoid", {"E": 16}, 333),
     "skew_E64": ("skew", {"E": 64, "hot_stride": 8}, 500),
     "skew_conc_E64": ("skew_conc", {"E": 64, "hot_stride": 8}, 300),
+    # wide gated shared expert: its dense GEMMs take the large-tile path
+    "shared_wide": ("tiny", {"D": 256, "E": 4, "K": 2, "F": 256, "F_shared": 2048,
+                             "shared_gated": True, "dtype": "bf16"}, 2048),
 }
 
 
@@ -148,3 +151,22 @@ def test_concentrated_routing_hits_eight_experts():
     counts = i64(r["expert_counts"])
     assert sorted(np.nonzero(counts)[0].tolist()) == hot_experts(cfg)
     assert np.all(counts[hot_experts(cfg)] == T)
+
+
+GROUPED_TILES = ["small", "large", "stream64", "stream128", "stream192"]
+
+
+@pytest.mark.parametrize("tile", GROUPED_TILES)
+@pytest.mark.parametrize("name", ["a3b_E16", "a17b_E32", "skew_conc_E64", "ds_sigmoid_E16",
+                                  "a3b_T1"])
+def test_every_grouped_tile_shape_matches_oracle(name, tile, monkeypatch):
+    """The library picks the grouped GEMM's tile from the mean rows per expert; forcing each
+    shape on the same inputs covers ragged groups, multi-tile experts and empty experts in all."""
+    monkeypatch.setenv("MOE_GROUPED_TILE", tile)
+    cfg, layer, T = _case(name)
+    for atomic in (False, True):
+        out32, r = _forward(cfg, layer, T, torch.float32, atomic)
+        ref = _oracle(cfg, layer, r["logits"])
+        _check_routing(cfg, r, ref)
+        err = rel_max_err(out32, ref["out"])
+        assert err <= _tol(cfg), f"{name}/{tile}/atomic={atomic}: max|err|/RMS = {err:.3e}"
