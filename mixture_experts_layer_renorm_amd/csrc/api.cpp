@@ -75,9 +75,19 @@ bool gated(const moe_problem* p) { return p->F_shared > 0 && p->shared_gated; }
 // expert; larger groups (and fp32) take the LDS tile GEMM.  MOE_GROUPED_TILE (small, large,
 // stream64, stream128, stream192) overrides the choice, for tuning and for tests that cover
 // every tile shape at small sizes; the streaming shapes apply to bf16 only.
+// The weight-streaming GEMM addresses its operands with 32-bit offsets from a uniform base:
+// token rows ([T*K, max(D, F)] at most, via x_perm or H) and one expert's weights must each
+// span less than 4 GiB.
+bool stream_fits(const moe_problem* p) {
+  const int64_t es = (int64_t)esize(p->dtype);
+  const int64_t wide = p->D > p->F ? p->D : p->F;
+  const int64_t lim = (int64_t)1 << 32;
+  return p->T * p->K * wide * es < lim && (int64_t)2 * p->F * p->D * es < lim;
+}
+
 moe::TileCfg grouped_cfg(const moe_problem* p) {
+  const bool bf = p->dtype == MOE_DTYPE_BF16 && stream_fits(p);
   if (const char* o = std::getenv("MOE_GROUPED_TILE")) {
-    const bool bf = p->dtype == MOE_DTYPE_BF16;
     if (!std::strcmp(o, "small")) return moe::TILE_SMALL;
     if (!std::strcmp(o, "large")) return moe::TILE_LARGE;
     if (bf && !std::strcmp(o, "stream64")) return moe::TILE_STREAM_64;
@@ -86,7 +96,7 @@ moe::TileCfg grouped_cfg(const moe_problem* p) {
   }
   const int64_t A = p->T * p->K;
   const double mean = (double)A / p->E;
-  if (p->dtype == MOE_DTYPE_BF16) {
+  if (bf) {
     if (mean <= 24) return moe::TILE_STREAM_64;
     if (mean <= 170) return moe::TILE_STREAM_192;
     return moe::TILE_LARGE;
