@@ -28,6 +28,7 @@
 //    N tile, then by M tile.  Tiles that share an expert's weights or rows therefore run at the
 //    same time on the same XCD and meet in its L2.
 #include "kernels.h"
+#include "silu.h"
 
 namespace moe {
 namespace {
@@ -56,7 +57,6 @@ __device__ __forceinline__ void barrier_after() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
 template <typename T>
 __device__ __forceinline__ T to_out(float v);
@@ -102,7 +102,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
   const int ncols = kSwiglu ? p.N : p.N + (p.B2 ? 1 : 0);
   constexpr int BNE = kSwiglu ? BN / 2 : BN;  // output columns per tile
   const int ntN = (ncols + BNE - 1) / BNE;
-  const int mt_total = p.tiles ? *p.tile_count : (p.M + BM - 1) / BM;
+  const int mt_total = p.tiles ? load_uniform(p.tile_count, 0) : (p.M + BM - 1) / BM;
   const int nt = mt_total * ntN;
   const int xcd = blockIdx.x % kXcds, per = gridDim.x / kXcds, jb = blockIdx.x / kXcds;
   const int lo = (int)((int64_t)nt * xcd / kXcds), hi = (int)((int64_t)nt * (xcd + 1) / kXcds);
@@ -125,8 +125,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
     const int q = t / ntN;
     int first, cnt;
     if (p.tiles) {
-      first = p.tiles[q * kTileStride + 4];
-      cnt = p.tiles[q * kTileStride + 5];
+      first = load_uniform(p.tiles, q * kTileStride + 4);
+      cnt = load_uniform(p.tiles, q * kTileStride + 5);
     } else {
       first = 0;
       cnt = mt_total;
@@ -136,9 +136,9 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
     const int m = first + l % cnt;
     int group, row_start, rows;
     if (p.tiles) {
-      group = p.tiles[m * kTileStride + 0];
-      row_start = p.tiles[m * kTileStride + 1];
-      rows = p.tiles[m * kTileStride + 2];
+      group = load_uniform(p.tiles, m * kTileStride + 0);
+      row_start = load_uniform(p.tiles, m * kTileStride + 1);
+      rows = load_uniform(p.tiles, m * kTileStride + 2);
     } else {
       group = 0;
       row_start = m * BM;
@@ -262,7 +262,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
             const int row = wm * WTM + i * 16 + lk * 4 + r;
             if (row < rows) {
               const float g = acc[i][j][r], u = acc[i][j + NI / 2][r];
-              H[(int64_t)(row_start + row) * p.ldc + n] = to_out<T>(silu_f(g) * u);
+              H[(int64_t)(row_start + row) * p.ldc + n] = to_out<T>(silu_fast(g) * u);
             }
           }
         }

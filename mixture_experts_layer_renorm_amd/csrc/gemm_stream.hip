@@ -2,24 +2,30 @@
 //
 // At the token counts of the layer's workloads an expert sees a few to a few hundred rows, so
 // the expert GEMMs are bound by reading the weights from HBM (read volume b_W·N_e·U:
-// "S23-J10" §3), not by the matrix cores.  Under full load HBM latency is several
-// microseconds, so what bounds throughput is how many weight bytes each CU keeps in flight.
-// LDS (160 KiB) is too small for that; the register file (512 KiB per CU) is not:
+// "S23-J10" §3), not by the matrix cores.  The kernel is built so that the memory pipeline of
+// each CU only carries what the product needs and always has enough of it in flight:
 //  * A work-group of 8 waves (two per SIMD) owns BN = 256 weight rows (output columns) of one
 //    expert and up to BM of its token rows, so every weight byte is fetched from HBM once.  The
 //    waves split the columns, 32 each, which keeps each wave's accumulators small.
-//  * Each lane loads its weight fragments with plain 16-byte vector loads straight into
-//    registers already in the MFMA operand layout (lane l: row l%16, k = 8*(l/16)..+7), P K-steps
-//    (of 32) ahead, in a register ring: 16 KiB of weights per step, P = 8 steps (128 KiB) in
-//    flight per CU.
-//  * The token rows, shared by all waves, are loaded the same P steps ahead into registers and
-//    written one step ahead of use into a double-buffered LDS tile of 64-byte rows whose 16-byte
-//    chunks are XOR-swizzled by (row >> 1) & 3 (conflict-free for the 16-row operand fetches).
-//  * Only ordinary vector loads are in flight, so the compiler's vmcnt accounting is exact
-//    across the unrolled ring (mixing them with LDS DMA makes it fall back to vmcnt(0)).
-//  * Epilogues: fused SiLU·up (gate_up; a wave's 64 columns are 32 gate/up pairs), fp32 row
-//    store (down), or the weighted fp32 atomic combine (down, opt-in).
+//  * A K step is 64 wide.  Each lane loads its weight fragments with plain 16-byte vector loads
+//    straight into registers in the MFMA operand layout (lane l: row l%16, k = 8*(l/16)..+7 of
+//    each 32-wide half); the two halves of a row's 128 bytes are requested back to back, so
+//    the second hits the line the first brought into L1.  A register ring holds P steps
+//    (P·32 KiB per CU) in flight.
+//  * Token rows, shared by all waves, are loaded with the same step into registers and written
+//    one step ahead of use into a double-buffered LDS tile of 128-byte rows whose 16-byte
+//    chunks are XOR-swizzled by (row >> 1) & 7 (conflict-free for the 16-row operand
+//    fetches).  Rows past the group's end are not fetched.
+//  * Only ordinary vector loads are in flight and every path into the K loop starts with
+//    none outstanding, so the compiler's load counts are exact across the ring.
+//  * When the step count is a multiple of P the ring runs on across tiles: the last round of a
+//    tile fetches the first P steps of the next, whose loads then overlap this tile's
+//    epilogue.
+//  * Epilogues: fused SiLU·up (gate_up; a wave's 32 columns are 16 gate/up pairs), fp32 row
+//    store (down), both staged in LDS and written as whole 16-byte chunks, or the weighted
+//    fp32 atomic combine (down, opt-in).
 #include "kernels.h"
+#include "silu.h"
 
 namespace moe {
 namespace {
@@ -27,9 +33,12 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRow = 64;  // LDS bytes per token row per step (32 bf16)
+constexpr int kRow = 128;  // bytes per token row per K step (64 bf16)
+// s_waitcnt immediate (gfx9 layout) that waits for vmcnt == 0 and leaves expcnt/lgkmcnt free.
+constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+// 16-byte chunk swizzle of a 128-byte LDS row.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // Token-row chunk i of a thread exists unless it falls in the partial last round (known at
 // compile time when CH is a multiple of the block size).
@@ -37,8 +46,6 @@ template <int CH, int NT, int LA>
 __device__ __forceinline__ bool a_live(int tid, int i) {
   return CH % NT == 0 || i + 1 < LA || tid + NT * i < CH;
 }
-
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
 // One output tile; every field is uniform across the work-group.
 struct StreamTile {
@@ -49,23 +56,25 @@ struct StreamTile {
 // entries [first, first + cnt) of the tile map and own logical tiles [first·ntN, (first+cnt)·ntN).
 __device__ __forceinline__ StreamTile decode_tile(const GemmParams& p, int t, int ntN) {
   const int q = t / ntN;
-  const int first = p.tiles[q * kTileStride + 4];
-  const int cnt = p.tiles[q * kTileStride + 5];
+  const int first = load_uniform(p.tiles, q * kTileStride + 4);
+  const int cnt = load_uniform(p.tiles, q * kTileStride + 5);
   const int l = t - first * ntN;
   const int m = first + l % cnt;
   StreamTile s;
   s.n_tile = l / cnt;
-  s.group = p.tiles[m * kTileStride + 0];
-  s.row_start = p.tiles[m * kTileStride + 1];
-  s.rows = p.tiles[m * kTileStride + 2];
+  s.group = load_uniform(p.tiles, m * kTileStride + 0);
+  s.row_start = load_uniform(p.tiles, m * kTileStride + 1);
+  s.rows = load_uniform(p.tiles, m * kTileStride + 2);
   return s;
 }
 
-// Source row of tile row r (rows past the group's end repeat its last row; their results are
-// discarded by the epilogue).
-__device__ __forceinline__ int token_row(const GemmParams& p, const StreamTile& s, int r) {
+// Source entry of tile row r: the gather-table entry (A row = entry / a_div) or the row itself.
+// Rows past the group's end repeat its last row; their results are discarded by the epilogue.
+// The division is left to the caller, so the gather load is not waited for until its row is
+// needed.
+__device__ __forceinline__ int token_src(const GemmParams& p, const StreamTile& s, int r) {
   const int pos = s.row_start + min(r, s.rows - 1);
-  return p.a_gather ? p.a_gather[pos] / p.a_div : pos;
+  return p.a_gather ? p.a_gather[pos] : pos;
 }
 
 template <int BM, int P, int EPI, bool CROSS>
@@ -74,10 +83,11 @@ __global__ void __launch_bounds__(512) stream_kernel(const GemmParams p) {
   constexpr int BN = 256;
   constexpr int MI = BM / 16;      // 16-row sub-tiles
   constexpr int NJ = 2;            // 16-column sub-tiles per wave
-  constexpr int CH = BM * 4;       // 16-byte token-row chunks per step
+  constexpr int KH = 2;            // 32-wide MFMA halves of a K step
+  constexpr int CH = BM * 8;       // 16-byte token-row chunks per step
   constexpr int LA = (CH + NT - 1) / NT;  // token-row loads per thread per step (last: partial)
   constexpr bool kSwiglu = EPI == EPI_SWIGLU;
-  static_assert(CH % 64 == 0, "a wave loads whole chunk groups");
+  static_assert(BM % 16 == 0 && CH % 64 == 0, "whole 16-row sub-tiles, whole-wave chunk groups");
 
   __shared__ __attribute__((aligned(16))) char smem[2][BM * kRow];
   // Epilogue staging: output rows are assembled in LDS and leave as whole 16-byte chunks.
@@ -95,45 +105,54 @@ __global__ void __launch_bounds__(512) stream_kernel(const GemmParams p) {
 
   constexpr int BNE = kSwiglu ? BN / 2 : BN;  // output columns per tile
   const int ntN = (p.N + BNE - 1) / BNE;
-  const int mt_total = *p.tile_count;
+  const int mt_total = load_uniform(p.tile_count, 0);
   const int nt = mt_total * ntN;
   const int xcd = blockIdx.x % kXcds, per = gridDim.x / kXcds, jb = blockIdx.x / kXcds;
   const int lo = (int)((int64_t)nt * xcd / kXcds), hi = (int)((int64_t)nt * (xcd + 1) / kXcds);
-  const int nk = p.Kdim / 32;
+  const int nk = p.Kdim / 64;
   int t = lo + jb;
   if (t >= hi) return;
 
-  // Token-row chunk i of this thread: c = tid + 512 i -> tile row c >> 2, LDS slot c & 3, which
-  // holds logical chunk (c & 3) ^ swz(row) of the row's 64 bytes.
-  int arow_t[LA], alds[LA], aoff[LA];
+  // Token-row chunk i of this thread: c = tid + 512 i -> tile row c >> 3, LDS slot c & 7, which
+  // holds logical chunk (c & 7) ^ swz(row) of the row's 128 bytes.  A wave's chunks cover 8
+  // consecutive rows starting at arow0[i] (uniform).
+  int arow_t[LA], alds[LA], aoff[LA], arow0[LA];
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
-    const int r = min((tid + NT * i) >> 2, BM - 1);
+    const int r = min((tid + NT * i) >> 3, BM - 1);
     arow_t[i] = r;
-    alds[i] = r * kRow + ((tid & 3) << 4);
-    aoff[i] = ((tid & 3) ^ swz(r)) << 4;
+    arow0[i] = (wave * 64 + NT * i) >> 3;
+    alds[i] = r * kRow + ((tid & 7) << 4);
+    aoff[i] = ((tid & 7) ^ swz(r)) << 4;
   }
 
   StreamTile cur = decode_tile(p, t, ntN);
   int arow[LA];
 #pragma unroll
-  for (int i = 0; i < LA; ++i) arow[i] = token_row(p, cur, arow_t[i]);
+  for (int i = 0; i < LA; ++i) arow[i] = token_src(p, cur, arow_t[i]);
 
   // Loaders: byte offsets of this thread's token-row chunks in A (aoffs) and of its weight rows
   // in the current group (boffs, from the uniform base bbase); all operands are below 4 GiB, so
-  // the loads take a scalar base plus a 32-bit lane offset.  With nk a multiple of P the ring
-  // runs on across tiles: the last P steps of a tile fetch the first P steps of the next, and
-  // the last step stages its first rows, so the next tile starts with its loads in flight while
-  // this one's epilogue stores drain.
+  // the loads take a scalar base plus a 32-bit lane offset.  ld_rows: rows of the tile being
+  // fetched (chunk groups past it are skipped).
   uint32_t aoffs[LA], boffs[NJ];
   const char* bbase;
-  bf16x8 areg[P][LA], breg[P][NJ];
+  int ld_rows;
+  bf16x8 areg[P][LA], breg[P][NJ][KH];
+  // token-row registers of skipped chunk groups keep whatever they held: start them defined
+#pragma unroll
+  for (int s_ = 0; s_ < P; ++s_)
+#pragma unroll
+    for (int i = 0; i < LA; ++i) areg[s_][i] = bf16x8{};
 
 #define MOE_STREAM_POINT(S)                                                                  \
   {                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < LA; ++i) aoffs[i] =                                \
-        (uint32_t)arow[i] * (uint32_t)p.lda_bytes + (uint32_t)aoff[i];                       \
+    _Pragma("unroll") for (int i = 0; i < LA; ++i) {                                         \
+      const int row_ = p.a_gather ? arow[i] / p.a_div : arow[i];                             \
+      aoffs[i] = (uint32_t)row_ * (uint32_t)p.lda_bytes + (uint32_t)aoff[i];                 \
+    }                                                                                        \
     bbase = p.B + (int64_t)(S).group * p.b_group_bytes;                                      \
+    ld_rows = (S).rows;                                                                      \
     _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                         \
       int wr;                                                                                \
       if (kSwiglu) { /* sub-tile 0: gate rows, sub-tile 1: the matching up rows */           \
@@ -151,10 +170,12 @@ __global__ void __launch_bounds__(512) stream_kernel(const GemmParams p) {
 #define MOE_STREAM_LOAD(SLOT, STEP)                                                          \
   {                                                                                          \
     const uint32_t off_ = (uint32_t)(STEP) * kRow;                                           \
-    _Pragma("unroll") for (int i = 0; i < LA; ++i) if (a_live<CH, NT, LA>(tid, i))           \
-        areg[SLOT][i] = *(const bf16x8*)(p.A + (aoffs[i] + off_));                           \
-    _Pragma("unroll") for (int j = 0; j < NJ; ++j) breg[SLOT][j] =                           \
-        *(const bf16x8*)(bbase + (boffs[j] + off_));                                         \
+    _Pragma("unroll") for (int i = 0; i < LA; ++i)                                           \
+        if (a_live<CH, NT, LA>(tid, i) && arow0[i] < ld_rows)                                \
+            areg[SLOT][i] = *(const bf16x8*)(p.A + (aoffs[i] + off_));                       \
+    _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                           \
+      _Pragma("unroll") for (int h = 0; h < KH; ++h) breg[SLOT][j][h] =                      \
+          *(const bf16x8*)(bbase + (boffs[j] + off_ + h * 64));                              \
   }
 
   MOE_STREAM_POINT(cur)
@@ -162,25 +183,25 @@ __global__ void __launch_bounds__(512) stream_kernel(const GemmParams p) {
   for (int s_ = 0; s_ < P; ++s_)
     if (s_ < nk) MOE_STREAM_LOAD(s_, s_)
 
-  // One K step: multiply LDS buffer ks&1 by weight slot QQ; if ISSUE, refill slot QQ with step
-  // ISTEP of the tile behind (AS, BS); if STAGE_NEXT, stage slot QQ+1's token rows into the
-  // other LDS buffer.
+  // One K step: multiply LDS buffer ks&1 by weight slot QQ (both 32-wide halves); if ISSUE,
+  // refill slot QQ with step ISTEP of the tile set up by MOE_STREAM_POINT; if STAGE_NEXT,
+  // stage slot QQ+1's token rows into the other LDS buffer.  Operand fragment u = h·MI + i is
+  // read from LDS two ahead of its MFMAs.
+#define MOE_STREAM_AFRAG(U)                                                                  \
+  (*(const bf16x8*)(sm + ((U) % MI * 16 + lr) * kRow +                                      \
+                    ((((U) / MI) * 4 + lk) ^ swz((U) % MI * 16 + lr)) * 16))
 #define MOE_STREAM_STEP(QQ, KS, ISSUE, ISTEP, STAGE_NEXT)                                  \
   {                                                                                        \
     const char* sm = smem[(KS) & 1];                                                       \
-    bf16x8 af[MI];                                                                         \
-    _Pragma("unroll") for (int i = 0; i < MI && i < 2; ++i) {                              \
-      const int r = i * 16 + lr;                                                           \
-      af[i] = *(const bf16x8*)(sm + r * kRow + ((lk ^ swz(r)) << 4));                      \
-    }                                                                                      \
-    _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                       \
-      if (i + 2 < MI) {                                                                    \
-        const int r = (i + 2) * 16 + lr;                                                   \
-        af[i + 2] = *(const bf16x8*)(sm + r * kRow + ((lk ^ swz(r)) << 4));                \
-      }                                                                                    \
+    bf16x8 af[KH * MI];                                                                    \
+    af[0] = MOE_STREAM_AFRAG(0);                                                           \
+    af[1] = MOE_STREAM_AFRAG(1);                                                           \
+    _Pragma("unroll") for (int u = 0; u < KH * MI; ++u) {                                  \
+      if (u + 2 < KH * MI) af[u + 2] = MOE_STREAM_AFRAG(u + 2);                            \
       __builtin_amdgcn_sched_barrier(0);                                                   \
-      _Pragma("unroll") for (int j = 0; j < NJ; ++j) acc[i][j] =                           \
-          __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], breg[QQ][j], acc[i][j], 0, 0, 0); \
+      _Pragma("unroll") for (int j = 0; j < NJ; ++j) acc[u % MI][j] =                      \
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u], breg[QQ][j][u / MI],              \
+                                                  acc[u % MI][j], 0, 0, 0);                \
       __builtin_amdgcn_sched_barrier(0);                                                   \
     }                                                                                      \
     if (ISSUE) MOE_STREAM_LOAD(QQ, ISTEP)                                                  \
@@ -191,15 +212,17 @@ __global__ void __launch_bounds__(512) stream_kernel(const GemmParams p) {
     __syncthreads();                                                                       \
   }
 
-  bool staged = false;  // step 0 of the current tile already sits in LDS buffer 0
-  for (;;) {
-    if (!staged) {
+  // Stage step 0 of the first tile.  Every tile then starts with nothing in flight (the
+  // prologue's loads may have been issued in any order, and the epilogue drains below): the
+  // compiler's load counts at the head of the K loop are only exact if every path into it
+  // agrees, and otherwise every round would wait for the whole ring.
 #pragma unroll
-      for (int i = 0; i < LA; ++i)
-        if (a_live<CH, NT, LA>(tid, i)) *(bf16x8*)(&smem[0][alds[i]]) = areg[0][i];
-      __syncthreads();
-    }
+  for (int i = 0; i < LA; ++i)
+    if (a_live<CH, NT, LA>(tid, i)) *(bf16x8*)(&smem[0][alds[i]]) = areg[0][i];
+  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
+  for (;;) {
     // the next tile and its token rows, fetched now so they have arrived before they are used
     const int tn = t + per;
     const bool more = tn < hi;
@@ -207,7 +230,7 @@ __global__ void __launch_bounds__(512) stream_kernel(const GemmParams p) {
     if (more) {
       nxt = decode_tile(p, tn, ntN);
 #pragma unroll
-      for (int i = 0; i < LA; ++i) arow[i] = token_row(p, nxt, arow_t[i]);
+      for (int i = 0; i < LA; ++i) arow[i] = token_src(p, nxt, arow_t[i]);
     }
 
     f32x4 acc[MI][NJ];
@@ -228,7 +251,6 @@ __global__ void __launch_bounds__(512) stream_kernel(const GemmParams p) {
 #pragma unroll
       for (int qq = 0; qq < P; ++qq)
         MOE_STREAM_STEP(qq, ks0 + qq, more, qq, (qq + 1 < P) || more);
-      staged = true;
     } else {
       // steady state: all P steps of a round issue step ks + P (needs ks + P < nk)
       int ks0 = 0;
@@ -250,7 +272,6 @@ __global__ void __launch_bounds__(512) stream_kernel(const GemmParams p) {
         for (int s_ = 0; s_ < P; ++s_)
           if (s_ < nk) MOE_STREAM_LOAD(s_, s_)
       }
-      staged = false;
     }
 
     // ---- epilogue ---------------------------------------------------------------------------
@@ -268,7 +289,7 @@ __global__ void __launch_bounds__(512) stream_kernel(const GemmParams p) {
         if (i * 16 < cur.rows) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            Eh[(i * 16 + elk * 4 + r) * kLdH + col] = (__bf16)(silu_f(acc[i][0][r]) * acc[i][1][r]);
+            Eh[(i * 16 + elk * 4 + r) * kLdH + col] = (__bf16)(silu_fast(acc[i][0][r]) * acc[i][1][r]);
         }
       }
       __syncthreads();
@@ -336,18 +357,30 @@ __global__ void __launch_bounds__(512) stream_kernel(const GemmParams p) {
           }
         }
     }
+    // Stores and loads retire out of order, so once the stores above are pending the compiler
+    // can no longer count the loads in flight and would drain the whole ring at the head of
+    // every round that follows.  One explicit drain here, when the next tile's first loads have
+    // had the epilogue's duration to land, keeps its counts exact for the rest of the tile.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     if (!more) break;
     cur = nxt;
     t = tn;
+    if constexpr (!CROSS) {  // stage the next tile's step 0 (its loads are in)
+#pragma unroll
+      for (int i = 0; i < LA; ++i)
+        if (a_live<CH, NT, LA>(tid, i)) *(bf16x8*)(&smem[0][alds[i]]) = areg[0][i];
+      __syncthreads();
+    }
   }
 #undef MOE_STREAM_STEP
+#undef MOE_STREAM_AFRAG
 #undef MOE_STREAM_POINT
 #undef MOE_STREAM_LOAD
 }
 
 template <int BM, int P, int EPI>
 hipError_t launch_epi(const GemmParams& p, dim3 g, hipStream_t stream) {
-  if ((p.Kdim / 32) % P == 0)
+  if ((p.Kdim / 64) % P == 0)
     hipLaunchKernelGGL((stream_kernel<BM, P, EPI, true>), g, dim3(512), 0, stream, p);
   else
     hipLaunchKernelGGL((stream_kernel<BM, P, EPI, false>), g, dim3(512), 0, stream, p);
@@ -383,11 +416,11 @@ hipError_t launch_stream_gemm(TileCfg cfg, Epilogue epi, const GemmParams& p, in
   if (max_mtiles <= 0) return hipSuccess;
   switch (cfg) {
     case TILE_STREAM_64:
-      return launch_bm<64, 8>(epi, p, max_mtiles, 1, stream);
+      return launch_bm<64, 4>(epi, p, max_mtiles, 1, stream);
     case TILE_STREAM_192:
-      return launch_bm<192, 4>(epi, p, max_mtiles, 1, stream);
+      return launch_bm<192, 2>(epi, p, max_mtiles, 1, stream);
     case TILE_STREAM_128:
-      return launch_bm<128, 8>(epi, p, max_mtiles, 1, stream);
+      return launch_bm<128, 4>(epi, p, max_mtiles, 1, stream);
     default:
       return hipErrorInvalidValue;
   }

@@ -11,6 +11,14 @@ constexpr int kXcds = 8;         // MI355X: 8 accelerator complex dies, 32 CUs e
 constexpr int kCus = 256;
 constexpr int kTileStride = 8;   // int32 words per tile-map entry
 
+// Reads a word that is the same for the whole work-group and is not written while the kernel
+// runs (tile maps and counts, produced by an earlier launch) through the scalar cache.  Read
+// with a vector load instead, the compiler's next wait on the vector-memory counter would also
+// wait for every weight load in flight.
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
 // Grouped / dense GEMM description.  C[row, n] = sum_k A[row, k] * B[n, k]; rows come from
 // per-group row ranges (tile map) or one dense range [0, M).
 enum Epilogue : int {
