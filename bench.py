@@ -26,7 +26,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PROFILES = os.path.join(ROOT, "profiles")
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_renorm_amd", "csrc", "gemm.hip")
+# sources the grouped streaming GEMM is compiled from (a traffic record is only used if it was
+# taken on exactly these)
+_CSRC = os.path.join(ROOT, "mixture_experts_layer_renorm_amd", "csrc")
+GEMM_SRCS = [os.path.join(_CSRC, f) for f in ("gemm_stream.hip", "kernels.h", "silu.h")]
+
+
+def gemm_source_sha256() -> str:
+    h = hashlib.sha256()
+    for f in GEMM_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def parse_args():
@@ -125,8 +135,8 @@ def run_workload(name, steps, warmup, atomic_combine, hip):
                           cfg.dtype, cfg.dtype)
     st = dict(zip(abi.MOE_STAGE_NAMES, stage_ms))
     res = {
-        "workload": name, "T": cfg.T, "D": cfg.D, "E": cfg.E, "K": cfg.K, "F": cfg.F,
-        "F_shared": cfg.F_shared, "scoring": cfg.scoring, "dtype": cfg.dtype,
+        "workload": name, "plan": abi.describe_plan(p), "T": cfg.T, "D": cfg.D, "E": cfg.E,
+        "K": cfg.K, "F": cfg.F, "F_shared": cfg.F_shared, "scoring": cfg.scoring, "dtype": cfg.dtype,
         "ms_per_step": ms_per_step, "gpu_ms_per_step": gpu_ms,
         "tokens_per_s": cfg.T / (ms_per_step / 1e3),
         "stage_ms": st, "U": U, "assignments": A,
@@ -166,8 +176,7 @@ def read_traffic(kernel_tag):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
-    if kv.get("gemm_source_sha256") != sha:
+    if kv.get("gemm_source_sha256") != gemm_source_sha256():
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -236,7 +245,8 @@ def main():
 
     gu = main_res["gate_up"]
     traffic = read_traffic(f"gate_up_{args.workload}")
-    roofline = {"kernel": "gemm_kernel<bf16,128,256,SWIGLU> (routed gate_up, fused SiLU*up)",
+    grouped = main_res["plan"].split("grouped gate_up/down: ")[1].split(";")[0]
+    roofline = {"kernel": f"routed gate_up, {grouped} tiles, fused SiLU*up epilogue",
                 "bound": "hbm", "achieved": gu["gbs"], "peak": costmodel.HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": gu["gbs"] / costmodel.HBM_PEAK_GBS, "traffic": traffic,
                 "alg_bytes_per_launch": gu["alg_bytes"], "avg_launch_ms": gu["ms"],

@@ -186,6 +186,11 @@ int moe_forward_timed(const moe_problem *p, const void *x, const moe_weights *w,
 /* Static text for a status code. */
 const char *moe_status_string(int status);
 
+/* Thread-local text naming the kernels moe_forward would launch for problem p (tile shapes
+ * of the router, grouped and shared GEMMs; combine mode), e.g. for reports.  Returns "" and
+ * sets moe_last_error() if p is invalid.  Valid until the next call on this thread. */
+const char *moe_describe_plan(const moe_problem *p);
+
 /* Thread-local detail about the last failed call on this thread ("" if none). */
 const char *moe_last_error(void);
 

@@ -32,7 +32,7 @@ MOE_FLAG_NO_RENORM = 2
 
 SYMBOLS = ("moe_workspace_size", "moe_route", "moe_route_logits", "moe_dispatch",
            "moe_experts", "moe_combine", "moe_forward", "moe_forward_timed",
-           "moe_status_string", "moe_last_error")
+           "moe_status_string", "moe_last_error", "moe_describe_plan")
 MOE_STAGE_NAMES = ("router", "topk", "dispatch", "gate_up", "shared", "down", "final")
 MOE_STAGE_COUNT = len(MOE_STAGE_NAMES)
 
@@ -98,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []
     lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_describe_plan.argtypes = [prob]
+    lib.moe_describe_plan.restype = ctypes.c_char_p
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -181,6 +183,15 @@ def _ws(ws: Optional[torch.Tensor]):
 
 
 # ---------------------------------------------------------------------- entry points ----
+
+def describe_plan(p: moe_problem) -> str:
+    """Names of the kernels moe_forward launches for p (tile shapes, combine mode)."""
+    lib = load_library()
+    text = lib.moe_describe_plan(ctypes.byref(p)).decode()
+    if not text:
+        raise MoEError(MOE_ERR_INVALID_ARG, lib.moe_last_error().decode())
+    return text
+
 
 def moe_workspace_size(p: moe_problem) -> int:
     lib = load_library()

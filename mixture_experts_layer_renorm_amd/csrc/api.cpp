@@ -322,6 +322,25 @@ const char* moe_status_string(int status) {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
+const char* moe_describe_plan(const moe_problem* p) {
+  static thread_local std::string text;
+  text.clear();
+  g_last_error.clear();
+  if (check_problem(p)) return text.c_str();
+  auto name = [](moe::TileCfg c) -> std::string {
+    const bool stream = c == moe::TILE_STREAM_64 || c == moe::TILE_STREAM_128 ||
+                        c == moe::TILE_STREAM_192;
+    return std::string(stream ? "stream " : "tile ") + std::to_string(moe::tile_bm(c)) + "x" +
+           std::to_string(moe::tile_bn(c));
+  };
+  text = "router: " + name(dense_cfg(p->T, p->E + (gated(p) ? 1 : 0))) +
+         "; grouped gate_up/down: " + name(grouped_cfg(p));
+  if (has_shared(p)) text += "; shared: " + name(dense_cfg(p->T, (int64_t)2 * p->F_shared));
+  text += (p->flags & MOE_FLAG_ATOMIC_COMBINE) ? "; combine: fp32 atomics in the down epilogue"
+                                               : "; combine: gather in slot order";
+  return text.c_str();
+}
+
 int moe_workspace_size(const moe_problem* p, size_t* bytes) {
   g_last_error.clear();
   int st = check_problem(p);

@@ -349,7 +349,9 @@ int tile_bm(TileCfg cfg) {
   }
   return 256;
 }
-int tile_bn(TileCfg) { return 128; }
+// Weight rows per tile (output columns; half of them for the fused gate/up epilogue of the
+// streaming GEMM).
+int tile_bn(TileCfg cfg) { return cfg >= TILE_STREAM_64 ? 256 : 128; }
 
 hipError_t launch_gemm(int dtype, TileCfg cfg, Epilogue epi, const GemmParams& p,
                        int64_t max_mtiles, hipStream_t stream) {
