@@ -37,6 +37,13 @@ CASES = {
     # wide gated shared expert: its dense GEMMs take the large-tile path
     "shared_wide": ("tiny", {"D": 256, "E": 4, "K": 2, "F": 256, "F_shared": 2048,
                              "shared_gated": True, "dtype": "bf16"}, 2048),
+    # degenerate routings: every expert selected (dense mixture), a single expert
+    "dense_K_eq_E": ("tiny", {"E": 8, "K": 8}, 77),
+    "single_expert": ("tiny", {"E": 1, "K": 1, "dtype": "bf16"}, 50),
+    # the largest E and K the library takes, with reduction lengths of one and two K steps
+    "max_E_K": ("a3b_prefill", {"D": 128, "E": 1024, "K": 64, "F": 64}, 40),
+    # reduction lengths that are not a multiple of the streaming ring, ragged N tiles
+    "odd_k": ("a3b_prefill", {"D": 192, "F": 320, "E": 16}, 300),
 }
 
 
@@ -158,7 +165,7 @@ GROUPED_TILES = ["small", "large", "stream64", "stream128", "stream192"]
 
 @pytest.mark.parametrize("tile", GROUPED_TILES)
 @pytest.mark.parametrize("name", ["a3b_E16", "a17b_E32", "skew_conc_E64", "ds_sigmoid_E16",
-                                  "a3b_T1"])
+                                  "a3b_T1", "odd_k"])
 def test_every_grouped_tile_shape_matches_oracle(name, tile, monkeypatch):
     """The library picks the grouped GEMM's tile from the mean rows per expert; forcing each
     shape on the same inputs covers ragged groups, multi-tile experts and empty experts in all."""

@@ -39,7 +39,7 @@ def _check_route(logits, K, scoring="softmax", renormalize=True, check_w=True):
 
 
 @pytest.mark.parametrize("E,K", [(8, 2), (256, 8), (512, 10), (256, 6), (5, 2), (1000, 7),
-                                 (64, 64), (8, 8), (1, 1), (130, 3)])
+                                 (64, 64), (8, 8), (1, 1), (130, 3), (1024, 64)])
 @pytest.mark.parametrize("scoring", ["softmax", "sigmoid"])
 def test_topk_random_logits(E, K, scoring):
     g = torch.Generator(device="cpu").manual_seed(E * 100 + K)
