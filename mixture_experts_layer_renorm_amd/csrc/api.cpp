@@ -93,21 +93,25 @@ moe::TileCfg grouped_cfg(const moe_problem* p) {
     if (bf && !std::strcmp(o, "stream64")) return moe::TILE_STREAM_64;
     if (bf && !std::strcmp(o, "stream128")) return moe::TILE_STREAM_128;
     if (bf && !std::strcmp(o, "stream192")) return moe::TILE_STREAM_192;
+    if (p->dtype == MOE_DTYPE_BF16 && !std::strcmp(o, "mfma")) return moe::TILE_MFMA;
   }
   const int64_t A = p->T * p->K;
   const double mean = (double)A / p->E;
   if (bf) {
     if (mean <= 24) return moe::TILE_STREAM_64;
     if (mean <= 170) return moe::TILE_STREAM_192;
-    return moe::TILE_LARGE;
+    return moe::TILE_MFMA;
   }
+  if (p->dtype == MOE_DTYPE_BF16) return mean <= 48 ? moe::TILE_SMALL : moe::TILE_MFMA;
   return mean <= 48 ? moe::TILE_SMALL : moe::TILE_LARGE;
 }
-// Dense GEMMs (router, shared expert): large tiles unless they would leave CUs idle.
-moe::TileCfg dense_cfg(int64_t M, int64_t N) {
+// Dense GEMMs: large tiles unless they would leave CUs idle.  The router (extra gate column,
+// column bias) stays on the tile GEMM; the shared expert's bf16 GEMMs take the MFMA GEMM.
+moe::TileCfg dense_cfg(int64_t M, int64_t N, int dtype = MOE_DTYPE_F32) {
   const int64_t bm = moe::tile_bm(moe::TILE_LARGE), bn = moe::tile_bn(moe::TILE_LARGE);
-  return ((M + bm - 1) / bm) * ((N + bn - 1) / bn) >= moe::kCus ? moe::TILE_LARGE
-                                                                  : moe::TILE_SMALL;
+  const bool big = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) >= moe::kCus;
+  if (!big) return moe::TILE_SMALL;
+  return dtype == MOE_DTYPE_BF16 ? moe::TILE_MFMA : moe::TILE_LARGE;
 }
 
 // Workspace layout: every region 256-byte aligned.
@@ -258,7 +262,7 @@ hipError_t run_down(const moe_problem* p, const void* H, const void* w_d, const 
 hipError_t run_shared(const moe_problem* p, const void* x, const moe_weights* w, void* Hs,
                       float* out, const float* row_scale, hipStream_t s) {
   const size_t es = esize(p->dtype);
-  const moe::TileCfg cfg = dense_cfg(p->T, (int64_t)2 * p->F_shared);
+  const moe::TileCfg cfg = dense_cfg(p->T, (int64_t)2 * p->F_shared, p->dtype);
   const int bm = moe::tile_bm(cfg);
   const int64_t mt = (p->T + bm - 1) / bm;
   moe::GemmParams g{};
@@ -330,12 +334,14 @@ const char* moe_describe_plan(const moe_problem* p) {
   auto name = [](moe::TileCfg c) -> std::string {
     const bool stream = c == moe::TILE_STREAM_64 || c == moe::TILE_STREAM_128 ||
                         c == moe::TILE_STREAM_192;
-    return std::string(stream ? "stream " : "tile ") + std::to_string(moe::tile_bm(c)) + "x" +
+    const char* kind = stream ? "stream " : c == moe::TILE_MFMA ? "mfma " : "tile ";
+    return std::string(kind) + std::to_string(moe::tile_bm(c)) + "x" +
            std::to_string(moe::tile_bn(c));
   };
   text = "router: " + name(dense_cfg(p->T, p->E + (gated(p) ? 1 : 0))) +
          "; grouped gate_up/down: " + name(grouped_cfg(p));
-  if (has_shared(p)) text += "; shared: " + name(dense_cfg(p->T, (int64_t)2 * p->F_shared));
+  if (has_shared(p))
+    text += "; shared: " + name(dense_cfg(p->T, (int64_t)2 * p->F_shared, p->dtype));
   text += (p->flags & MOE_FLAG_ATOMIC_COMBINE) ? "; combine: fp32 atomics in the down epilogue"
                                                : "; combine: gather in slot order";
   return text.c_str();

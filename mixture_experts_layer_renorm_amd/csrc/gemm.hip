@@ -346,16 +346,21 @@ int tile_bm(TileCfg cfg) {
     case TILE_STREAM_64: return 64;
     case TILE_STREAM_192: return 192;
     case TILE_STREAM_128: return 128;
+    case TILE_MFMA: return 256;
   }
   return 256;
 }
 // Weight rows per tile (output columns; half of them for the fused gate/up epilogue of the
 // streaming GEMM).
-int tile_bn(TileCfg cfg) { return cfg >= TILE_STREAM_64 ? 256 : 128; }
+int tile_bn(TileCfg cfg) { return cfg >= TILE_STREAM_64 ? 256 : 128; }  // incl. TILE_MFMA
 
 hipError_t launch_gemm(int dtype, TileCfg cfg, Epilogue epi, const GemmParams& p,
                        int64_t max_mtiles, hipStream_t stream) {
   if (max_mtiles <= 0) return hipSuccess;
+  if (cfg == TILE_MFMA) {
+    if (dtype != 1) return hipErrorInvalidValue;
+    return launch_mfma_gemm(epi, p, max_mtiles, stream);
+  }
   if (cfg >= TILE_STREAM_64) return launch_stream_gemm(cfg, epi, p, max_mtiles, stream);
   // Occupancy from LDS: SMALL stages 4 x 20 KiB (2 work-groups per CU), LARGE 3 x 48 KiB (1).
   // LARGE is 256 rows x 128 columns: one M tile holds every row of an expert with up to 256

@@ -64,6 +64,7 @@ enum TileCfg : int {
   TILE_STREAM_64 = 2,   // weight-streaming GEMM, BM=64 (decode-sized groups), bf16 only
   TILE_STREAM_192 = 3,  // weight-streaming GEMM, BM=192, bf16 only
   TILE_STREAM_128 = 4,  // weight-streaming GEMM, BM=128, bf16 only
+  TILE_MFMA = 5,        // matrix-core-bound GEMM, 256 x 256 tiles, bf16 only, no B2 / col_bias
 };
 int tile_bm(TileCfg cfg);
 int tile_bn(TileCfg cfg);
@@ -71,6 +72,10 @@ int tile_bn(TileCfg cfg);
 // Grouped weight-streaming GEMM (tile map required, no B2 column), bf16.
 hipError_t launch_stream_gemm(TileCfg cfg, Epilogue epi, const GemmParams& p, int64_t max_mtiles,
                               hipStream_t stream);
+
+// Matrix-core-bound grouped or dense GEMM (256 x 256 tiles), bf16.
+hipError_t launch_mfma_gemm(Epilogue epi, const GemmParams& p, int64_t max_mtiles,
+                            hipStream_t stream);
 
 // dtype: 0 = fp32, 1 = bf16.  Returns hipSuccess or the launch error.
 hipError_t launch_gemm(int dtype, TileCfg cfg, Epilogue epi, const GemmParams& p, int64_t max_tiles,
