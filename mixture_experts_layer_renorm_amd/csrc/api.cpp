@@ -70,14 +70,17 @@ bool has_shared(const moe_problem* p) { return p->F_shared > 0; }
 bool gated(const moe_problem* p) { return p->F_shared > 0 && p->shared_gated; }
 
 // Grouped (routed-expert) GEMMs.  The host does not see the per-expert counts (no sync), so the
-// tile is chosen from the mean rows per expert A/E.  bf16 groups of up to ~170 rows are bound by
-// weight reads and take the weight-streaming GEMM with an M tile that holds a whole typical
-// expert; larger groups (and fp32) take the LDS tile GEMM.  MOE_GROUPED_TILE (small, large,
-// stream64, stream128, stream192) overrides the choice, for tuning and for tests that cover
-// every tile shape at small sizes; the streaming shapes apply to bf16 only.
-// The weight-streaming GEMM addresses its operands with 32-bit offsets from a uniform base:
-// token rows ([T*K, max(D, F)] at most, via x_perm or H) and one expert's weights must each
-// span less than 4 GiB.
+// dispatch kernel sorts the experts into two tile maps on the device: experts with up to 192
+// rows are bound by reading their weights and go to the weight-streaming GEMM (64-row M tiles
+// when the mean group is decode-sized, 192 otherwise); larger groups reuse each weight byte
+// hundreds of times and go to the matrix-core GEMM (256 x 256 tiles).  No expert can have
+// more than T rows, so for T <= 192 the second map is not built.  fp32 layers (and operands
+// of 4 GiB or more) use the tile GEMM with one map.  MOE_GROUPED_TILE (small, large, stream64,
+// stream128, stream192, mfma) forces one map with the named tile, for tuning and for tests
+// that cover every tile shape at small sizes; the streaming and MFMA shapes apply to bf16 only.
+// The streaming and matrix-core GEMMs address their operands with 32-bit offsets from a
+// uniform base: token rows ([T*K, max(D, F)] at most, via x_perm or H) and one expert's weights
+// must each span less than 4 GiB.
 bool stream_fits(const moe_problem* p) {
   const int64_t es = (int64_t)esize(p->dtype);
   const int64_t wide = p->D > p->F ? p->D : p->F;
@@ -85,26 +88,38 @@ bool stream_fits(const moe_problem* p) {
   return p->T * p->K * wide * es < lim && (int64_t)2 * p->F * p->D * es < lim;
 }
 
-moe::TileCfg grouped_cfg(const moe_problem* p) {
+struct GroupedPlan {
+  moe::TileCfg cfg0, cfg1;
+  int split;  // < 0: one map
+};
+
+GroupedPlan grouped_plan(const moe_problem* p) {
   const bool bf = p->dtype == MOE_DTYPE_BF16 && stream_fits(p);
   if (const char* o = std::getenv("MOE_GROUPED_TILE")) {
-    if (!std::strcmp(o, "small")) return moe::TILE_SMALL;
-    if (!std::strcmp(o, "large")) return moe::TILE_LARGE;
-    if (bf && !std::strcmp(o, "stream64")) return moe::TILE_STREAM_64;
-    if (bf && !std::strcmp(o, "stream128")) return moe::TILE_STREAM_128;
-    if (bf && !std::strcmp(o, "stream192")) return moe::TILE_STREAM_192;
-    if (p->dtype == MOE_DTYPE_BF16 && !std::strcmp(o, "mfma")) return moe::TILE_MFMA;
+    if (!std::strcmp(o, "small")) return {moe::TILE_SMALL, moe::TILE_SMALL, -1};
+    if (!std::strcmp(o, "large")) return {moe::TILE_LARGE, moe::TILE_LARGE, -1};
+    if (bf && !std::strcmp(o, "stream64")) return {moe::TILE_STREAM_64, moe::TILE_STREAM_64, -1};
+    if (bf && !std::strcmp(o, "stream128"))
+      return {moe::TILE_STREAM_128, moe::TILE_STREAM_128, -1};
+    if (bf && !std::strcmp(o, "stream192"))
+      return {moe::TILE_STREAM_192, moe::TILE_STREAM_192, -1};
+    if (bf && !std::strcmp(o, "mfma")) return {moe::TILE_MFMA, moe::TILE_MFMA, -1};
   }
   const int64_t A = p->T * p->K;
   const double mean = (double)A / p->E;
   if (bf) {
-    if (mean <= 24) return moe::TILE_STREAM_64;
-    if (mean <= 170) return moe::TILE_STREAM_192;
-    return moe::TILE_MFMA;
+    const moe::TileCfg small = mean <= 24 ? moe::TILE_STREAM_64 : moe::TILE_STREAM_192;
+    if (p->T <= 192) return {small, small, -1};
+    return {small, moe::TILE_MFMA, 192};
   }
-  if (p->dtype == MOE_DTYPE_BF16) return mean <= 48 ? moe::TILE_SMALL : moe::TILE_MFMA;
-  return mean <= 48 ? moe::TILE_SMALL : moe::TILE_LARGE;
+  const moe::TileCfg c = mean <= 48 ? moe::TILE_SMALL : moe::TILE_LARGE;
+  return {c, c, -1};
 }
+
+moe::TileSplit tile_split(const GroupedPlan& g, int64_t max_mtiles) {
+  return {moe::tile_bm(g.cfg0), moe::tile_bm(g.cfg1), g.split, max_mtiles};
+}
+
 // Dense GEMMs: large tiles unless they would leave CUs idle.  The router (extra gate column,
 // column bias) stays on the tile GEMM; the shared expert's bf16 GEMMs take the MFMA GEMM.
 moe::TileCfg dense_cfg(int64_t M, int64_t N, int dtype = MOE_DTYPE_F32) {
@@ -144,7 +159,7 @@ Layout layout(const moe_problem* p) {
   L.perm = take((size_t)A * 4);
   L.inv_perm = take((size_t)A * 4);
   L.seg_counts = take((size_t)moe::dispatch_num_segments(A) * E * 4);
-  L.tiles = take((size_t)L.max_mtiles * moe::kTileStride * 4);
+  L.tiles = take((size_t)2 * L.max_mtiles * moe::kTileStride * 4);  // two maps
   L.tile_count = take(16);
   L.H = take((size_t)A * p->F * es);
   L.Hs = take((size_t)T * p->F_shared * es);
@@ -209,9 +224,22 @@ hipError_t run_router(const moe_problem* p, const void* x, const moe_weights* w,
 }
 
 // gate_up over the tile map: rows gathered from x through perm (or read from x_perm).
+// Launches a grouped GEMM over map 0 and, if the plan splits, map 1.
+hipError_t launch_grouped(const moe_problem* p, const GroupedPlan& plan, moe::Epilogue epi,
+                          moe::GemmParams g, const int32_t* tiles, const int32_t* tile_count,
+                          int64_t max_mtiles, hipStream_t s) {
+  g.tiles = tiles;
+  g.tile_count = tile_count;
+  hipError_t e = moe::launch_gemm(p->dtype, plan.cfg0, epi, g, max_mtiles, s);
+  if (e != hipSuccess || plan.split < 0) return e;
+  g.tiles = tiles + max_mtiles * moe::kTileStride;
+  g.tile_count = tile_count + 1;
+  return moe::launch_gemm(p->dtype, plan.cfg1, epi, g, max_mtiles, s);
+}
+
 hipError_t run_gate_up(const moe_problem* p, const void* x, const void* x_perm, const void* w_gu,
                        const int32_t* perm, const int32_t* tiles, const int32_t* tile_count,
-                       int64_t max_mtiles, void* H, moe::TileCfg cfg, hipStream_t s) {
+                       int64_t max_mtiles, void* H, const GroupedPlan& plan, hipStream_t s) {
   const size_t es = esize(p->dtype);
   moe::GemmParams g{};
   g.A = (const char*)(x_perm ? x_perm : x);
@@ -223,15 +251,13 @@ hipError_t run_gate_up(const moe_problem* p, const void* x, const void* x_perm, 
   g.ldb_bytes = (int64_t)p->D * es;
   g.N = p->F;
   g.Kdim = p->D;
-  g.tiles = tiles;
-  g.tile_count = tile_count;
   g.C = H;
   g.ldc = p->F;
-  return moe::launch_gemm(p->dtype, cfg, moe::EPI_SWIGLU, g, max_mtiles, s);
+  return launch_grouped(p, plan, moe::EPI_SWIGLU, g, tiles, tile_count, max_mtiles, s);
 }
 
 hipError_t run_down(const moe_problem* p, const void* H, const void* w_d, const int32_t* tiles,
-                    const int32_t* tile_count, int64_t max_mtiles, moe::TileCfg cfg,
+                    const int32_t* tile_count, int64_t max_mtiles, const GroupedPlan& plan,
                     float* y_perm, float* acc, const int32_t* perm, const float* topk_w,
                     hipStream_t s) {
   const size_t es = esize(p->dtype);
@@ -243,19 +269,17 @@ hipError_t run_down(const moe_problem* p, const void* H, const void* w_d, const 
   g.ldb_bytes = (int64_t)p->F * es;
   g.N = p->D;
   g.Kdim = p->F;
-  g.tiles = tiles;
-  g.tile_count = tile_count;
   if (y_perm) {
     g.C = y_perm;
     g.ldc = p->D;
-    return moe::launch_gemm(p->dtype, cfg, moe::EPI_STORE, g, max_mtiles, s);
+    return launch_grouped(p, plan, moe::EPI_STORE, g, tiles, tile_count, max_mtiles, s);
   }
   g.acc_out = acc;
   g.ldo = p->D;
   g.perm = perm;
   g.topk_w = topk_w;
   g.topk = p->K;
-  return moe::launch_gemm(p->dtype, cfg, moe::EPI_ATOMIC_COMBINE, g, max_mtiles, s);
+  return launch_grouped(p, plan, moe::EPI_ATOMIC_COMBINE, g, tiles, tile_count, max_mtiles, s);
 }
 
 // Shared expert on all T tokens: Hs = SwiGLU gate/up of x; out = row_scale * (Hs Ws_downᵀ).
@@ -339,7 +363,10 @@ const char* moe_describe_plan(const moe_problem* p) {
            std::to_string(moe::tile_bn(c));
   };
   text = "router: " + name(dense_cfg(p->T, p->E + (gated(p) ? 1 : 0))) +
-         "; grouped gate_up/down: " + name(grouped_cfg(p));
+         "; grouped gate_up/down: " + name(grouped_plan(p).cfg0);
+  if (grouped_plan(p).split >= 0)
+    text += " (experts with <= " + std::to_string(grouped_plan(p).split) + " rows), " +
+            name(grouped_plan(p).cfg1) + " (larger)";
   if (has_shared(p))
     text += "; shared: " + name(dense_cfg(p->T, (int64_t)2 * p->F_shared, p->dtype));
   text += (p->flags & MOE_FLAG_ATOMIC_COMBINE) ? "; combine: fp32 atomics in the down epilogue"
@@ -422,8 +449,8 @@ int moe_dispatch(const moe_problem* p, const void* x, moe_routing* r, void* x_pe
   hipStream_t s = (hipStream_t)stream;
   const int64_t A = p->T * p->K;
   MOE_HIP_TRY(moe::launch_dispatch(r->topk_idx, A, p->E, at<int32_t>(workspace, L.seg_counts),
-                                   r->expert_counts, r->expert_offsets, r->perm, r->inv_perm, 32,
-                                   nullptr, nullptr, s),
+                                   r->expert_counts, r->expert_offsets, r->perm, r->inv_perm,
+                                   moe::TileSplit{32, 32, -1, 0}, nullptr, nullptr, s),
               "dispatch launch");
   if (x_perm)
     MOE_HIP_TRY(moe::launch_gather_rows(x, p->D, (int)esize(p->dtype), r->perm, r->expert_offsets,
@@ -452,17 +479,17 @@ int moe_experts(const moe_problem* p, const void* x, const void* x_perm, const m
   Layout L;
   if ((st = check_ws(p, workspace, workspace_bytes, &L))) return st;
   hipStream_t s = (hipStream_t)stream;
-  const moe::TileCfg cfg = grouped_cfg(p);
-  const int bm = moe::tile_bm(cfg);
+  const GroupedPlan plan = grouped_plan(p);
   int32_t* tiles = at<int32_t>(workspace, L.tiles);
   int32_t* tile_count = at<int32_t>(workspace, L.tile_count);
-  MOE_HIP_TRY(moe::launch_tile_map(r->expert_offsets, p->E, bm, tiles, tile_count, s),
+  MOE_HIP_TRY(moe::launch_tile_map(r->expert_offsets, p->E, tile_split(plan, L.max_mtiles), tiles,
+                                   tile_count, s),
               "tile map launch");
   void* H = at<void>(workspace, L.H);
   MOE_HIP_TRY(run_gate_up(p, x, x_perm, w->w_gate_up, r->perm, tiles, tile_count, L.max_mtiles, H,
-                          cfg, s),
+                          plan, s),
               "gate_up GEMM launch");
-  MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, cfg, y_perm, nullptr,
+  MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, plan, y_perm, nullptr,
                        nullptr, nullptr, s),
               "down GEMM launch");
   if (has_shared(p) && y_shared)
@@ -551,20 +578,19 @@ int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_
                                g ? gate_logit : nullptr, g ? r.shared_gate : nullptr, s),
               "top-K launch");
   // 2. dispatch + tile map
-  const moe::TileCfg cfg = grouped_cfg(p);
-  const int bm = moe::tile_bm(cfg);
+  const GroupedPlan plan = grouped_plan(p);
   int32_t* tiles = at<int32_t>(ws, L.tiles);
   int32_t* tile_count = at<int32_t>(ws, L.tile_count);
   MOE_HIP_TRY(mark(MOE_STAGE_DISPATCH), "event record");
   MOE_HIP_TRY(moe::launch_dispatch(r.topk_idx, A, p->E, at<int32_t>(ws, L.seg_counts),
-                                   r.expert_counts, r.expert_offsets, r.perm, r.inv_perm, bm, tiles,
-                                   tile_count, s),
+                                   r.expert_counts, r.expert_offsets, r.perm, r.inv_perm,
+                                   tile_split(plan, L.max_mtiles), tiles, tile_count, s),
               "dispatch launch");
   // 3. routed gate_up with SiLU*up
   void* H = at<void>(ws, L.H);
   MOE_HIP_TRY(mark(MOE_STAGE_GATE_UP), "event record");
   MOE_HIP_TRY(run_gate_up(p, x, nullptr, w->w_gate_up, r.perm, tiles, tile_count, L.max_mtiles, H,
-                          cfg, s),
+                          plan, s),
               "gate_up GEMM launch");
   const float* gate = g ? r.shared_gate : nullptr;
   if (!(p->flags & MOE_FLAG_ATOMIC_COMBINE)) {
@@ -576,7 +602,7 @@ int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_
       MOE_HIP_TRY(run_shared(p, x, w, at<void>(ws, L.Hs), y_shared, nullptr, s),
                   "shared expert launch");
     MOE_HIP_TRY(mark(MOE_STAGE_DOWN), "event record");
-    MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, cfg, y_perm, nullptr,
+    MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, plan, y_perm, nullptr,
                          nullptr, nullptr, s),
                 "down GEMM launch");
     MOE_HIP_TRY(mark(MOE_STAGE_FINAL), "event record");
@@ -595,8 +621,8 @@ int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_
   else
     MOE_HIP_TRY(moe::launch_zero(acc, p->T * p->D, s), "zero launch");
   MOE_HIP_TRY(mark(MOE_STAGE_DOWN), "event record");
-  MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, cfg, nullptr, acc, r.perm,
-                       r.topk_w, s),
+  MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, plan, nullptr, acc,
+                       r.perm, r.topk_w, s),
               "down GEMM launch");
   MOE_HIP_TRY(mark(MOE_STAGE_FINAL), "event record");
   if (p->out_dtype != MOE_DTYPE_F32)

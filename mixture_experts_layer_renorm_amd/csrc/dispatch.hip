@@ -83,20 +83,26 @@ __global__ void __launch_bounds__(256) count_kernel(const int32_t* __restrict__ 
   for (int e = lane; e < E; e += 64) seg_counts[seg * E + e] = hist[e];
 }
 
-// Builds the tile map from per-expert counts held in LDS.  One entry per M tile:
-// {expert, first row position, rows, 0, first M tile of the expert, M tiles of the expert}.
-__device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, int bm, int* scratch,
-                            int32_t* tiles, int32_t* tile_count) {
-  int total = 0;
+// Builds the tile maps from per-expert counts held in LDS.  One entry per M tile:
+// {expert, first row position, rows, 0, first M tile of the expert, M tiles of the expert};
+// experts with more than ts.split rows go to map 1 (bm1-row tiles), the others to map 0.
+__device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, const TileSplit ts,
+                            int* scratch, int32_t* tiles, int32_t* tile_count) {
+  int32_t* maps[2] = {tiles, tiles + ts.map1_entries * kTileStride};
+  const int bms[2] = {ts.bm0, ts.bm1};
+  int total[2] = {0, 0};
   for (int base = 0; base < E; base += kScanThreads) {
     const int e = base + threadIdx.x;
     const int c = e < E ? cnt_lds[e] : 0;
-    const int mt = (c + bm - 1) / bm;
-    int chunk_total;
-    const int first = block_exclusive_scan(mt, scratch, &chunk_total) + total;
-    if (e < E) {
+    const int which = (ts.split >= 0 && c > ts.split) ? 1 : 0;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int bm = bms[m];
+      const int mt = which == m ? (c + bm - 1) / bm : 0;
+      int chunk_total;
+      const int first = block_exclusive_scan(mt, scratch, &chunk_total) + total[m];
       for (int q = 0; q < mt; ++q) {
-        int32_t* ent = tiles + (int64_t)(first + q) * kTileStride;
+        int32_t* ent = maps[m] + (int64_t)(first + q) * kTileStride;
         ent[0] = e;
         ent[1] = off_lds[e] + q * bm;
         ent[2] = min(bm, c - q * bm);
@@ -106,16 +112,20 @@ __device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, int b
         ent[6] = 0;
         ent[7] = 0;
       }
+      total[m] += chunk_total;
     }
-    total += chunk_total;
   }
-  if (threadIdx.x == 0) *tile_count = total;
+  if (threadIdx.x == 0) {
+    tile_count[0] = total[0];
+    tile_count[1] = total[1];
+  }
 }
 
 __global__ void __launch_bounds__(kScanThreads) scan_kernel(int32_t* __restrict__ seg_counts,
                                                             int64_t nseg, int E,
                                                             int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ offsets, int bm,
+                                                            int32_t* __restrict__ offsets,
+                                                            const TileSplit ts,
                                                             int32_t* __restrict__ tiles,
                                                             int32_t* __restrict__ tile_count) {
   extern __shared__ int sm[];
@@ -175,11 +185,11 @@ __global__ void __launch_bounds__(kScanThreads) scan_kernel(int32_t* __restrict_
   }
   if (threadIdx.x == 0) offsets[E] = total;
   __syncthreads();
-  if (tiles) build_tiles(cnt, off, E, bm, scratch, tiles, tile_count);
+  if (tiles) build_tiles(cnt, off, E, ts, scratch, tiles, tile_count);
 }
 
 __global__ void __launch_bounds__(kScanThreads) tile_map_kernel(const int32_t* __restrict__ offsets,
-                                                                int E, int bm,
+                                                                int E, const TileSplit ts,
                                                                 int32_t* __restrict__ tiles,
                                                                 int32_t* __restrict__ tile_count) {
   extern __shared__ int sm[];
@@ -191,7 +201,7 @@ __global__ void __launch_bounds__(kScanThreads) tile_map_kernel(const int32_t* _
     cnt[e] = offsets[e + 1] - offsets[e];
   }
   __syncthreads();
-  build_tiles(cnt, off, E, bm, scratch, tiles, tile_count);
+  build_tiles(cnt, off, E, ts, scratch, tiles, tile_count);
 }
 
 __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ idx, int64_t A,
@@ -265,7 +275,8 @@ int64_t dispatch_num_segments(int64_t A) { return (A + kSegLen - 1) / kSegLen; }
 
 hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_counts,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                           int bm, int32_t* tiles, int32_t* tile_count, hipStream_t stream) {
+                           const TileSplit& ts, int32_t* tiles, int32_t* tile_count,
+                           hipStream_t stream) {
   const int64_t nseg = dispatch_num_segments(A);
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
@@ -276,7 +287,7 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_co
   if (err != hipSuccess) return err;
   const size_t lds_scan = (size_t)(2 * E + kScanThreads + 32) * sizeof(int);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), lds_scan, stream, seg_counts, nseg,
-                     E, counts, offsets, bm, tiles, tile_count);
+                     E, counts, offsets, ts, tiles, tile_count);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(scatter_kernel, g, b, lds_waves, stream, idx, A, E, nbits, nseg, seg_counts,
@@ -284,10 +295,10 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_co
   return hipGetLastError();
 }
 
-hipError_t launch_tile_map(const int32_t* offsets, int E, int bm, int32_t* tiles,
+hipError_t launch_tile_map(const int32_t* offsets, int E, const TileSplit& ts, int32_t* tiles,
                            int32_t* tile_count, hipStream_t stream) {
   const size_t lds = (size_t)(2 * E + 32) * sizeof(int);
-  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(kScanThreads), lds, stream, offsets, E, bm,
+  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(kScanThreads), lds, stream, offsets, E, ts,
                      tiles, tile_count);
   return hipGetLastError();
 }

@@ -86,14 +86,23 @@ hipError_t launch_topk(const float* logits, int64_t T, int E, int K, int scoring
                        int32_t* idx, float* w, const float* gate_logit, float* gate_out,
                        hipStream_t stream);
 
+// Tiling of the grouped GEMMs.  Experts with at most `split` rows are tiled with bm0-row M
+// tiles into map 0, larger ones with bm1-row tiles into map 1 (written map1_entries entries
+// after map 0); split < 0 puts every expert in map 0.  tile_count[0..1] receive the sizes.
+struct TileSplit {
+  int bm0, bm1, split;
+  int64_t map1_entries;
+};
+
 // Dispatch.
 int dispatch_segment_len(int64_t A);
 int64_t dispatch_num_segments(int64_t A);
 hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_counts,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                           int bm, int32_t* tiles, int32_t* tile_count, hipStream_t stream);
-// Tile map from offsets alone (staged API).
-hipError_t launch_tile_map(const int32_t* offsets, int E, int bm, int32_t* tiles,
+                           const TileSplit& ts, int32_t* tiles, int32_t* tile_count,
+                           hipStream_t stream);
+// Tile maps from offsets alone (staged API).
+hipError_t launch_tile_map(const int32_t* offsets, int E, const TileSplit& ts, int32_t* tiles,
                            int32_t* tile_count, hipStream_t stream);
 hipError_t launch_gather_rows(const void* x, int64_t D, int esize, const int32_t* perm,
                               const int32_t* offsets, int E, int K, int64_t A, void* x_perm,
