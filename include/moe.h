@@ -178,7 +178,8 @@ enum {
 /* moe_forward with timing: events[i] (a caller-created hipEvent_t, passed as void*) is
  * recorded on `stream` right before stage i is launched and events[MOE_STAGE_COUNT] after
  * the last one, so hipEventElapsedTime(events[i], events[i+1]) brackets stage i.  `events`
- * must hold MOE_STAGE_COUNT + 1 valid events.  Same results and errors as moe_forward. */
+ * must hold MOE_STAGE_COUNT + 1 entries; a NULL entry is not recorded (so a caller can bracket
+ * one stage with two events).  Same results and errors as moe_forward. */
 int moe_forward_timed(const moe_problem *p, const void *x, const moe_weights *w,
                       moe_routing *r_opt, void *out, void *workspace, size_t workspace_bytes,
                       moe_stream_t stream, void *const *events);

@@ -35,6 +35,7 @@ SYMBOLS = ("moe_workspace_size", "moe_route", "moe_route_logits", "moe_dispatch"
            "moe_status_string", "moe_last_error", "moe_describe_plan")
 MOE_STAGE_NAMES = ("router", "topk", "dispatch", "gate_up", "shared", "down", "final")
 MOE_STAGE_COUNT = len(MOE_STAGE_NAMES)
+MOE_STAGE_GATE_UP = MOE_STAGE_NAMES.index("gate_up")
 
 _DTYPE_CODE = {torch.float32: MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16}
 _DTYPE_OF_CODE = {MOE_DTYPE_F32: torch.float32, MOE_DTYPE_BF16: torch.bfloat16}
@@ -261,7 +262,8 @@ def moe_forward(p: moe_problem, x: torch.Tensor, weights: Dict, routing: Optiona
 
 def moe_forward_timed(p: moe_problem, x: torch.Tensor, weights: Dict, routing: Optional[Dict],
                       out: torch.Tensor, workspace: torch.Tensor, events, stream=None) -> None:
-    """moe_forward recording `events` (MOE_STAGE_COUNT + 1 raw hipEvent_t handles as ints)."""
+    """moe_forward recording `events` (MOE_STAGE_COUNT + 1 raw hipEvent_t handles as ints;
+    None entries are not recorded)."""
     lib = load_library()
     if len(events) != MOE_STAGE_COUNT + 1:
         raise ValueError(f"need {MOE_STAGE_COUNT + 1} events")

@@ -120,7 +120,15 @@ moe::TileSplit tile_split(const GroupedPlan& g, int64_t max_mtiles) {
   return {moe::tile_bm(g.cfg0), moe::tile_bm(g.cfg1), g.split, max_mtiles};
 }
 
-// Dense GEMMs: large tiles unless they would leave CUs idle.  The router (extra gate column,
+// Router: bf16 batches of up to 1024 tokens use the split-K matrix-core router (partial sums
+// reduced by the top-K kernel), which keeps the latency of a short batch low; larger batches
+// and fp32 layers use the tile GEMM (one slice).
+bool router_split(const moe_problem* p) { return p->dtype == MOE_DTYPE_BF16 && p->T <= 1024; }
+int router_ks(const moe_problem* p) {
+  return router_split(p) ? moe::router_kslices(p->T, p->D, p->E, gated(p) ? 1 : 0) : 1;
+}
+
+// Dense GEMMs: large tiles unless they would leave CUs idle.  The fp32 router (extra gate column,
 // column bias) stays on the tile GEMM; the shared expert's bf16 GEMMs take the MFMA GEMM.
 moe::TileCfg dense_cfg(int64_t M, int64_t N, int dtype = MOE_DTYPE_F32) {
   const int64_t bm = moe::tile_bm(moe::TILE_LARGE), bn = moe::tile_bn(moe::TILE_LARGE);
@@ -149,7 +157,11 @@ Layout layout(const moe_problem* p) {
     return at;
   };
   L.max_mtiles = (A + 31) / 32 + (E < A ? E : A);  // upper bound for the smallest BM (32)
-  L.logits = take((size_t)T * E * 4);
+  {  // router output: logits [T, E], or the split-K partial sums [ks][T][E + gated]
+    const size_t ks = (size_t)router_ks(p);
+    const size_t a = (size_t)T * E * 4, b = ks * (size_t)T * (E + (gated(p) ? 1 : 0)) * 4;
+    L.logits = take(a > b ? a : b);
+  }
   L.gate_logit = take((size_t)T * 4);
   L.gate = take((size_t)T * 4);
   L.topk_idx = take((size_t)A * 4);
@@ -202,8 +214,27 @@ int check_ws(const moe_problem* p, void* ws, size_t bytes, Layout* L) {
 
 // ---- stage bodies (arguments already validated) -----------------------------------------
 
-hipError_t run_router(const moe_problem* p, const void* x, const moe_weights* w, float* logits,
-                      float* gate_logit, const void* gate_w, hipStream_t s) {
+// Router logits (and the shared-gate logit), left where launch_topk's arguments say.
+hipError_t run_router(const moe_problem* p, const void* x, const moe_weights* w, float* part,
+                      float* gate_logit, bool want_gate, moe::TopkArgs* ta, hipStream_t s) {
+  const void* gate_w = want_gate ? w->ws_gate : nullptr;
+  ta->T = p->T;
+  ta->E = p->E;
+  ta->K = p->K;
+  ta->scoring = p->scoring;
+  ta->renorm = !(p->flags & MOE_FLAG_NO_RENORM);
+  ta->src = part;
+  if (router_split(p)) {
+    const int ks = router_ks(p);
+    const int64_t ne = p->E + (gate_w ? 1 : 0);
+    ta->ks = ks;
+    ta->ld = ne;
+    ta->slice_stride = p->T * ne;
+    ta->gate_src = gate_w ? part + p->E : nullptr;
+    ta->gate_ld = ne;
+    return moe::launch_router_bf16(x, w->w_router, gate_w, w->logit_bias, p->T, p->D, p->E, ks,
+                                   part, s);
+  }
   const size_t es = esize(p->dtype);
   moe::GemmParams g{};
   g.A = (const char*)x;
@@ -214,10 +245,15 @@ hipError_t run_router(const moe_problem* p, const void* x, const moe_weights* w,
   g.N = p->E;
   g.Kdim = p->D;
   g.M = (int32_t)p->T;
-  g.C = logits;
+  g.C = part;
   g.ldc = p->E;
-  g.C2 = gate_logit;
+  g.C2 = gate_w ? gate_logit : nullptr;
   g.col_bias = w->logit_bias;
+  ta->ks = 1;
+  ta->ld = p->E;
+  ta->slice_stride = 0;
+  ta->gate_src = gate_w ? gate_logit : nullptr;
+  ta->gate_ld = 1;
   const moe::TileCfg cfg = dense_cfg(p->T, p->E + (gate_w ? 1 : 0));
   const int bm = moe::tile_bm(cfg);
   return moe::launch_gemm(p->dtype, cfg, moe::EPI_STORE, g, (p->T + bm - 1) / bm, s);
@@ -362,7 +398,12 @@ const char* moe_describe_plan(const moe_problem* p) {
     return std::string(kind) + std::to_string(moe::tile_bm(c)) + "x" +
            std::to_string(moe::tile_bn(c));
   };
-  text = "router: " + name(dense_cfg(p->T, p->E + (gated(p) ? 1 : 0))) +
+  const std::string router =
+      router_split(p)
+          ? "split-K mfma 16x64, " + std::to_string(router_ks(p)) + " K slice(s)"
+          : name(dense_cfg(p->T, p->E + (gated(p) ? 1 : 0)));
+  text = "router: " + router + "; dispatch: " +
+         (moe::dispatch_fused(p->T * p->K, p->E) ? "one work-group" : "count/scan/scatter") +
          "; grouped gate_up/down: " + name(grouped_plan(p).cfg0);
   if (grouped_plan(p).split >= 0)
     text += " (experts with <= " + std::to_string(grouped_plan(p).split) + " rows), " +
@@ -399,17 +440,16 @@ int moe_route(const moe_problem* p, const void* x, const moe_weights* w, moe_rou
   Layout L;
   if ((st = check_ws(p, workspace, workspace_bytes, &L))) return st;
   hipStream_t s = (hipStream_t)stream;
-  float* logits = r->logits ? r->logits : at<float>(workspace, L.logits);
   const bool want_gate = gated(p) && r->shared_gate;
-  float* gate_logit = at<float>(workspace, L.gate_logit);
-  MOE_HIP_TRY(run_router(p, x, w, logits, want_gate ? gate_logit : nullptr,
-                         want_gate ? w->ws_gate : nullptr, s),
+  moe::TopkArgs ta{};
+  MOE_HIP_TRY(run_router(p, x, w, at<float>(workspace, L.logits),
+                         at<float>(workspace, L.gate_logit), want_gate, &ta, s),
               "router GEMM launch");
-  MOE_HIP_TRY(moe::launch_topk(logits, p->T, p->E, p->K, p->scoring,
-                               !(p->flags & MOE_FLAG_NO_RENORM), r->topk_idx, r->topk_w,
-                               want_gate ? gate_logit : nullptr,
-                               want_gate ? r->shared_gate : nullptr, s),
-              "top-K launch");
+  ta.idx = r->topk_idx;
+  ta.w = r->topk_w;
+  ta.logits_out = r->logits;
+  ta.gate_out = want_gate ? r->shared_gate : nullptr;
+  MOE_HIP_TRY(moe::launch_topk(ta, s), "top-K launch");
   return MOE_OK;
 }
 
@@ -423,10 +463,18 @@ int moe_route_logits(const moe_problem* p, const float* logits, moe_routing* r,
   if (!r) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
   MOE_CHECK_PTR(r->topk_idx, "topk_idx");
   MOE_CHECK_PTR(r->topk_w, "topk_w");
-  MOE_HIP_TRY(moe::launch_topk(logits, p->T, p->E, p->K, p->scoring,
-                               !(p->flags & MOE_FLAG_NO_RENORM), r->topk_idx, r->topk_w, nullptr,
-                               nullptr, (hipStream_t)stream),
-              "top-K launch");
+  moe::TopkArgs ta{};
+  ta.src = logits;
+  ta.ks = 1;
+  ta.ld = p->E;
+  ta.T = p->T;
+  ta.E = p->E;
+  ta.K = p->K;
+  ta.scoring = p->scoring;
+  ta.renorm = !(p->flags & MOE_FLAG_NO_RENORM);
+  ta.idx = r->topk_idx;
+  ta.w = r->topk_w;
+  MOE_HIP_TRY(moe::launch_topk(ta, (hipStream_t)stream), "top-K launch");
   return MOE_OK;
 }
 
@@ -551,7 +599,6 @@ int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_
   Layout L;
   if ((st = check_ws(p, workspace, workspace_bytes, &L))) return st;
   void* ws = workspace;
-  if (!r.logits) r.logits = at<float>(ws, L.logits);
   if (!r.topk_idx) r.topk_idx = at<int32_t>(ws, L.topk_idx);
   if (!r.topk_w) r.topk_w = at<float>(ws, L.topk_w);
   if (!r.expert_counts) r.expert_counts = at<int32_t>(ws, L.counts);
@@ -565,18 +612,20 @@ int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_
   const bool g = gated(p);
   float* gate_logit = at<float>(ws, L.gate_logit);
   auto mark = [&](int stage) -> hipError_t {
-    return events ? hipEventRecord((hipEvent_t)events[stage], s) : hipSuccess;
+    return events && events[stage] ? hipEventRecord((hipEvent_t)events[stage], s) : hipSuccess;
   };
 
   // 1. router GEMM (+ shared-gate column) and top-K
   MOE_HIP_TRY(mark(MOE_STAGE_ROUTER), "event record");
-  MOE_HIP_TRY(run_router(p, x, w, r.logits, g ? gate_logit : nullptr, g ? w->ws_gate : nullptr, s),
+  moe::TopkArgs ta{};
+  MOE_HIP_TRY(run_router(p, x, w, at<float>(ws, L.logits), gate_logit, g, &ta, s),
               "router GEMM launch");
   MOE_HIP_TRY(mark(MOE_STAGE_TOPK), "event record");
-  MOE_HIP_TRY(moe::launch_topk(r.logits, p->T, p->E, p->K, p->scoring,
-                               !(p->flags & MOE_FLAG_NO_RENORM), r.topk_idx, r.topk_w,
-                               g ? gate_logit : nullptr, g ? r.shared_gate : nullptr, s),
-              "top-K launch");
+  ta.idx = r.topk_idx;
+  ta.w = r.topk_w;
+  ta.logits_out = r.logits;  // only if the caller asked for them
+  ta.gate_out = g ? r.shared_gate : nullptr;
+  MOE_HIP_TRY(moe::launch_topk(ta, s), "top-K launch");
   // 2. dispatch + tile map
   const GroupedPlan plan = grouped_plan(p);
   int32_t* tiles = at<int32_t>(ws, L.tiles);
@@ -647,11 +696,6 @@ int moe_forward_timed(const moe_problem* p, const void* x, const moe_weights* w,
     g_last_error.clear();
     return fail(MOE_ERR_INVALID_ARG, "events is NULL");
   }
-  for (int i = 0; i <= MOE_STAGE_COUNT; ++i)
-    if (!events[i]) {
-      g_last_error.clear();
-      return fail(MOE_ERR_INVALID_ARG, "events[%d] is NULL", i);
-    }
   return forward_impl(p, x, w, r_opt, out, workspace, workspace_bytes, stream, events);
 }
 

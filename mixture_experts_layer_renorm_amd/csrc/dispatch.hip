@@ -15,6 +15,9 @@
 //             lower-numbered peers plus the running position of its expert (in LDS) is its
 //             output position.  Segments, rounds and lanes all follow ascending a, so the sort
 //             is stable and the result bit-exact.
+#include <cstdlib>
+#include <cstring>
+
 #include "kernels.h"
 
 namespace moe {
@@ -23,6 +26,9 @@ namespace {
 constexpr int kScanThreads = 1024;
 constexpr int kSegRounds = 16;               // 64-id rounds per segment
 constexpr int kSegLen = 64 * kSegRounds;      // assignments per segment (one wave)
+// Single-work-group dispatch up to this many assignments (its LDS holds 18 ints per expert).
+constexpr int64_t kFusedMaxA = 8192;
+constexpr int kFusedMaxE = 768;
 
 __device__ __forceinline__ int wave_prefix_exclusive(int v, int lane) {
   int x = v;
@@ -252,6 +258,106 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
   }
 }
 
+// Whole dispatch in one work-group, for batches whose launch latency would otherwise dominate:
+// wave w owns the contiguous range [w*L, (w+1)*L) of assignment ids.  Count (LDS atomics into
+// the wave's own histogram), exclusive prefix over waves per expert, expert offsets, tile maps,
+// then the same ballot-ranked stable scatter as scatter_kernel.  Wave ranges, rounds and lanes
+// all follow ascending a, so the result equals the multi-kernel path's bit for bit.
+constexpr int kFusedWaves = kScanThreads / 64;
+constexpr int kFusedBatch = 8;  // 64-id rounds whose loads are issued together
+
+__global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
+    const int32_t* __restrict__ idx, int64_t A, int E, int nbits, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    const TileSplit ts, int32_t* __restrict__ tiles, int32_t* __restrict__ tile_count) {
+  extern __shared__ int sm[];
+  int* hist = sm;                       // [kFusedWaves][E]: counts, then running positions
+  int* cnt = hist + kFusedWaves * E;    // [E]
+  int* off = cnt + E;                   // [E]
+  int* scratch = off + E;               // [32]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t L = ((A + kFusedWaves - 1) / kFusedWaves + 63) / 64 * 64;
+  const int64_t a_begin = wave * L, a_end = min(A, a_begin + L);
+  int* h = hist + wave * E;
+  for (int e = lane; e < E; e += 64) h[e] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  for (int64_t b0 = a_begin; b0 < a_end; b0 += 64 * kFusedBatch) {
+    int ev[kFusedBatch];
+#pragma unroll
+    for (int r = 0; r < kFusedBatch; ++r) {
+      const int64_t a = b0 + r * 64 + lane;
+      ev[r] = a < a_end ? idx[a] : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < kFusedBatch; ++r)
+      if (ev[r] >= 0 && ev[r] < E) atomicAdd(&h[ev[r]], 1);
+  }
+  __syncthreads();
+  // per expert: each wave's first position within the expert, and the expert's count
+  for (int e = threadIdx.x; e < E; e += kScanThreads) {
+    int run = 0;
+    for (int w = 0; w < kFusedWaves; ++w) {
+      const int c = hist[w * E + e];
+      hist[w * E + e] = run;
+      run += c;
+    }
+    cnt[e] = run;
+  }
+  __syncthreads();
+  int total = 0;
+  for (int base = 0; base < E; base += kScanThreads) {
+    const int ee = base + threadIdx.x;
+    const int v = ee < E ? cnt[ee] : 0;
+    int chunk_total;
+    const int ex = block_exclusive_scan(v, scratch, &chunk_total) + total;
+    if (ee < E) {
+      off[ee] = ex;
+      counts[ee] = v;
+      offsets[ee] = ex;
+    }
+    total += chunk_total;
+  }
+  if (threadIdx.x == 0) offsets[E] = total;
+  __syncthreads();
+  if (tiles) build_tiles(cnt, off, E, ts, scratch, tiles, tile_count);
+  for (int i = threadIdx.x; i < kFusedWaves * E; i += kScanThreads) hist[i] += off[i % E];
+  __syncthreads();
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t b0 = a_begin; b0 < a_end; b0 += 64 * kFusedBatch) {
+    int ev[kFusedBatch];
+#pragma unroll
+    for (int r = 0; r < kFusedBatch; ++r) {
+      const int64_t a = b0 + r * 64 + lane;
+      ev[r] = a < a_end ? idx[a] : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < kFusedBatch; ++r) {
+      const int64_t a = b0 + r * 64 + lane;
+      const int e = ev[r];
+      const bool valid = e >= 0 && e < E;
+      unsigned long long peers = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const unsigned long long m = __ballot(bit);
+        peers &= bit ? m : ~m;
+      }
+      if (valid) {
+        const int rank = __popcll(peers & lt);
+        const int base = h[e];
+        const int pos = base + rank;
+        perm[pos] = (int32_t)a;
+        inv_perm[a] = pos;
+        if (rank == 0) h[e] = base + __popcll(peers);
+      } else if (a < a_end) {
+        inv_perm[a] = -1;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
 template <typename V>
 __global__ void __launch_bounds__(256) gather_rows_kernel(const V* __restrict__ x, int64_t vrow,
                                                           const int32_t* __restrict__ perm,
@@ -271,6 +377,15 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(const V* __restrict__ 
 
 int dispatch_segment_len(int64_t) { return kSegLen; }
 
+bool dispatch_fused(int64_t A, int E) {
+  bool fused = A <= kFusedMaxA && E <= kFusedMaxE;
+  if (const char* o = std::getenv("MOE_DISPATCH")) {
+    if (!std::strcmp(o, "fused")) fused = E <= kFusedMaxE;
+    if (!std::strcmp(o, "multi")) fused = false;
+  }
+  return fused;
+}
+
 int64_t dispatch_num_segments(int64_t A) { return (A + kSegLen - 1) / kSegLen; }
 
 hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_counts,
@@ -280,6 +395,12 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_co
   const int64_t nseg = dispatch_num_segments(A);
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
+  if (dispatch_fused(A, E)) {
+    const size_t lds = (size_t)((kFusedWaves + 2) * E + 32) * sizeof(int);
+    hipLaunchKernelGGL(dispatch_fused_kernel, dim3(1), dim3(kScanThreads), lds, stream, idx, A,
+                       E, nbits, counts, offsets, perm, inv_perm, ts, tiles, tile_count);
+    return hipGetLastError();
+  }
   const dim3 g((unsigned)((nseg + 3) / 4)), b(256);
   const size_t lds_waves = (size_t)4 * E * sizeof(int);
   hipLaunchKernelGGL(count_kernel, g, b, lds_waves, stream, idx, A, E, nseg, seg_counts);

@@ -81,10 +81,32 @@ hipError_t launch_mfma_gemm(Epilogue epi, const GemmParams& p, int64_t max_mtile
 hipError_t launch_gemm(int dtype, TileCfg cfg, Epilogue epi, const GemmParams& p, int64_t max_tiles,
                        hipStream_t stream);
 
-// Router top-K: logits [T, E] fp32 -> idx/w [T, K]; optional gate logits [T] -> sigmoid.
-hipError_t launch_topk(const float* logits, int64_t T, int E, int K, int scoring, int renorm,
-                       int32_t* idx, float* w, const float* gate_logit, float* gate_out,
-                       hipStream_t stream);
+// Router top-K.  The logit of (t, e) is the sum, in slice order, of src[q * slice_stride +
+// t * ld + e] over q < ks (ks = 1: src is the logits matrix).  Writes idx/w [T, K]; optionally
+// the summed logits [T, E] to logits_out, and sigmoid of the gate logit (same summation over
+// gate_src[q * slice_stride + t * gate_ld]) to gate_out [T].
+struct TopkArgs {
+  const float* src;
+  int ks;
+  int64_t slice_stride;
+  int64_t ld;
+  int64_t T;
+  int E, K, scoring, renorm;
+  int32_t* idx;
+  float* w;
+  float* logits_out;
+  const float* gate_src;
+  int64_t gate_ld;
+  float* gate_out;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+
+// Router logits from bf16 x [T, D] and W_r [E, D] (+ gate row [D]): K split into ks slices,
+// part [ks][T][E + gated] fp32, bias added in slice 0.
+int router_kslices(int64_t T, int D, int E, int gated);
+hipError_t launch_router_bf16(const void* x, const void* w_router, const void* w_gate,
+                              const float* bias, int64_t T, int D, int E, int ks, float* part,
+                              hipStream_t stream);
 
 // Tiling of the grouped GEMMs.  Experts with at most `split` rows are tiled with bm0-row M
 // tiles into map 0, larger ones with bm1-row tiles into map 1 (written map1_entries entries
@@ -97,6 +119,9 @@ struct TileSplit {
 // Dispatch.
 int dispatch_segment_len(int64_t A);
 int64_t dispatch_num_segments(int64_t A);
+// True when launch_dispatch runs as one work-group (small batches; MOE_DISPATCH=fused|multi
+// overrides).
+bool dispatch_fused(int64_t A, int E);
 hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_counts,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                            const TileSplit& ts, int32_t* tiles, int32_t* tile_count,

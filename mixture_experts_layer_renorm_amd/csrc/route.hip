@@ -43,29 +43,42 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+constexpr int kMaxSlices = 8;  // router K slices summed by the top-K kernel
+
 template <int NPL>  // logits held per lane: ceil(E / 64)
-__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int64_t T,
-                                                   int E, int K, int scoring, int renorm,
-                                                   int32_t* __restrict__ idx, float* __restrict__ w,
-                                                   const float* __restrict__ gate_logit,
-                                                   float* __restrict__ gate_out) {
+__global__ void __launch_bounds__(256) topk_kernel(const TopkArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + t * E;
+  if (t >= a.T) return;
+  const int E = a.E, K = a.K;
 
+  // logit e = the router's partial sums over K slices, added in slice order
   unsigned long long key[NPL];
   float val[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int e = lane + 64 * j;
+    float v = 0.0f;
     if (e < E) {
-      val[j] = row[e];
-      key[j] = ((unsigned long long)order_key(val[j]) << 32) | (0xFFFFFFFFu - (uint32_t)e);
-    } else {
-      val[j] = 0.0f;
-      key[j] = 0ull;  // below every real key
+      // all slices are loaded before the first add (clamped, always valid indices)
+      const float* p0 = a.src + t * a.ld + e;
+      if (a.ks == 1) {
+        v = p0[0];
+      } else {
+        float u[kMaxSlices];
+#pragma unroll
+        for (int q = 0; q < kMaxSlices; ++q)
+          u[q] = p0[(q < a.ks ? q : a.ks - 1) * a.slice_stride];
+        v = u[0];
+#pragma unroll
+        for (int q = 1; q < kMaxSlices; ++q)
+          if (q < a.ks) v += u[q];
+      }
+      if (a.logits_out) a.logits_out[t * E + e] = v;
     }
+    val[j] = v;
+    key[j] = e < E ? ((unsigned long long)order_key(v) << 32) | (0xFFFFFFFFu - (uint32_t)e)
+                   : 0ull;  // below every real key
   }
 
   // Slot k (k < K <= 64) is kept by lane k: its logit and expert id.
@@ -91,11 +104,11 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   }
 
   float s = 0.0f;
-  if (lane < K) s = scoring == 0 ? expf(my_val - top) : 1.0f / (1.0f + expf(-my_val));
+  if (lane < K) s = a.scoring == 0 ? expf(my_val - top) : 1.0f / (1.0f + expf(-my_val));
   float denom;
-  if (renorm) {
+  if (a.renorm) {
     denom = wave_sum(s);
-  } else if (scoring == 0) {
+  } else if (a.scoring == 0) {
     float part = 0.0f;
 #pragma unroll
     for (int j = 0; j < NPL; ++j)
@@ -105,24 +118,116 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     denom = 1.0f;
   }
   if (lane < K) {
-    idx[t * K + lane] = my_id;
-    w[t * K + lane] = s / denom;
+    a.idx[t * K + lane] = my_id;
+    a.w[t * K + lane] = s / denom;
   }
-  if (gate_out && lane == 0) gate_out[t] = 1.0f / (1.0f + expf(-gate_logit[t]));
+  if (a.gate_out && lane == 0) {
+    float g = a.gate_src[t * a.gate_ld];
+    for (int q = 1; q < a.ks; ++q) g += a.gate_src[q * a.slice_stride + t * a.gate_ld];
+    a.gate_out[t] = 1.0f / (1.0f + expf(-g));
+  }
+}
+
+// Router logits for bf16 operands, one K slice per blockIdx.z:
+//   part[z][t][n] = sum over k in slice z of x[t, k] * W[n, k]  (+ bias[n] in slice 0)
+// where W rows [0, E) are the router and row E (if gated) is the shared-expert gate vector.
+// A work-group computes 16 tokens x 64 columns; its 4 waves take every fourth 32-wide K step
+// of the slice and their sums are added in wave order through LDS.  Operands are read straight
+// from global memory into registers in the MFMA operand layout (lane l: row l % 16,
+// k = 8 (l / 16) .. +7 of a step).  Rows past T and columns past NE are computed on clamped,
+// valid rows and not stored.  Built for small token counts, where the latency of a long K
+// loop on few work-groups would dominate.
+__global__ void __launch_bounds__(256) router_kernel(const __bf16* __restrict__ x,
+                                                     const __bf16* __restrict__ wr,
+                                                     const __bf16* __restrict__ wg,
+                                                     const float* __restrict__ bias, int64_t T,
+                                                     int D, int E, int NE, int kslice,
+                                                     float* __restrict__ part) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __shared__ f32x4 red[3][4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lk = lane >> 4;
+  const int64_t tok0 = (int64_t)blockIdx.x * 16;
+  const int col0 = blockIdx.y * 64;
+  const int z = blockIdx.z;
+  const int64_t k0 = (int64_t)z * kslice + wave * 32 + lk * 8;
+  const int64_t trow = tok0 + lr < T ? tok0 + lr : T - 1;
+  const __bf16* ap = x + trow * D + k0;
+  const __bf16* bp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = col0 + 16 * j + lr;
+    bp[j] = (n < E ? wr + (int64_t)n * D : (n == E && wg) ? wg : wr) + k0;
+  }
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int kw = kslice - wave * 32;  // this wave's steps: k = 0, 128, ... < kw
+#pragma unroll 4
+  for (int k = 0; k < kw; k += 128) {
+    const bf16x8 av = *(const bf16x8*)(ap + k);
+    bf16x8 bv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[j] = *(const bf16x8*)(bp[j] + k);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[j], acc[j], 0, 0, 0);
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red[wave - 1][j][lane] = acc[j];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += red[w][j][lane];
+  // lane holds rows 4 (l / 16) + r, column l % 16 of each 16 x 16 sub-tile
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = col0 + 16 * j + lr;
+    if (n >= NE) continue;
+    const float b = (z == 0 && bias && n < E) ? bias[n] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = tok0 + lk * 4 + r;
+      if (t < T) part[((int64_t)z * T + t) * NE + n] = acc[j][r] + b;
+    }
+  }
 }
 
 }  // namespace
 
-hipError_t launch_topk(const float* logits, int64_t T, int E, int K, int scoring, int renorm,
-                       int32_t* idx, float* w, const float* gate_logit, float* gate_out,
-                       hipStream_t stream) {
+int router_kslices(int64_t T, int D, int E, int gated) {
+  const int64_t blocks = ((T + 15) / 16) * ((E + gated + 63) / 64);
+  int ks = 1;
+  // split K until about 256 work-groups run, keeping slices at least 256 wide
+  while (ks * 2 <= kMaxSlices && blocks * ks * 2 <= 256 && D % (ks * 2 * 32) == 0 &&
+         D / (ks * 2) >= 256)
+    ks *= 2;
+  return ks;
+}
+
+hipError_t launch_router_bf16(const void* x, const void* w_router, const void* w_gate,
+                              const float* bias, int64_t T, int D, int E, int ks, float* part,
+                              hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  dim3 g((unsigned)((T + 3) / 4)), b(256);
-  const int npl = (E + 63) / 64;
-#define MOE_TOPK_CASE(N)                                                                      \
-  case N:                                                                                     \
-    hipLaunchKernelGGL(topk_kernel<N>, g, b, 0, stream, logits, T, E, K, scoring, renorm, idx, \
-                       w, gate_logit, gate_out);                                              \
+  const int NE = E + (w_gate ? 1 : 0);
+  const dim3 g((unsigned)((T + 15) / 16), (unsigned)((NE + 63) / 64), (unsigned)ks), b(256);
+  hipLaunchKernelGGL(router_kernel, g, b, 0, stream, (const __bf16*)x, (const __bf16*)w_router,
+                     (const __bf16*)w_gate, bias, T, D, E, NE, D / ks, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
+  if (a.T <= 0) return hipSuccess;
+  dim3 g((unsigned)((a.T + 3) / 4)), b(256);
+  const int npl = (a.E + 63) / 64;
+#define MOE_TOPK_CASE(N)                                              \
+  case N:                                                             \
+    hipLaunchKernelGGL(topk_kernel<N>, g, b, 0, stream, a);           \
     break;
   switch (npl) {
     MOE_TOPK_CASE(1)

@@ -87,3 +87,17 @@ def test_dispatch_deterministic():
     b, _ = _run_dispatch(idx, 512)
     for k in ("expert_counts", "expert_offsets", "perm", "inv_perm"):
         assert torch.equal(a[k], b[k])
+
+
+# Both dispatch implementations (one work-group for small batches; count/scan/scatter kernels
+# otherwise) forced on the same inputs, inside and outside their default ranges.
+@pytest.mark.parametrize("path", ["fused", "multi"])
+@pytest.mark.parametrize("T,E,K", [(1, 1, 1), (64, 256, 8), (1023, 7, 3), (4096, 256, 8),
+                                   (2000, 768, 9), (20000, 64, 64)])
+def test_dispatch_both_paths(monkeypatch, path, T, E, K):
+    monkeypatch.setenv("MOE_DISPATCH", path)
+    g = torch.Generator().manual_seed(100 + T + E + K)
+    idx = _topk_like(T, E, K, g)
+    if T > 1:
+        idx[torch.rand(idx.shape, generator=g) < 0.05] = -1  # sentinels
+    _check(idx, E)

@@ -95,8 +95,13 @@ def _fp32_logit_bound(X, W, logits64):
     return gamma * (np.abs(X) @ np.abs(W).T) + 2 * u * np.abs(logits64) + 1e-30
 
 
+# bf16 batches of up to 1024 tokens take the split-K router (K slices summed by the top-K
+# kernel: 8 slices at T=64, 4 for the gated 513-column a17b router at T=70, 1 past 256 blocks);
+# larger batches and fp32 take the tile GEMM.
 @pytest.mark.parametrize("name,T", [("tiny", 64), ("a3b_prefill", 333), ("a17b", 70),
-                                    ("skew", 200), ("ds_sigmoid", 90)])
+                                    ("skew", 200), ("ds_sigmoid", 90), ("a3b_decode", 64),
+                                    ("a3b_prefill", 1), ("a17b", 1), ("a3b_prefill", 1024),
+                                    ("a3b_prefill", 1025)])
 def test_router_gemm_and_topk(name, T):
     cfg = CONFIGS[name]
     # only the router's tensors, drawn on the CPU at the workload's real widths
