@@ -48,6 +48,9 @@ def parse_args():
     ap.add_argument("--decode-workload", default="a3b_decode")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-granularity", action="store_true",
+                    help="skip the granularity pair (128 experts x F=1536 x top-8 vs "
+                         "64 x 3072 x top-4)")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--atomic-combine", action="store_true",
                     help="time the fused fp32-atomic combine instead of the default gather")
@@ -256,6 +259,23 @@ def main():
                                     args.atomic_combine, hip)
         sys.stderr.write(json.dumps({"progress": "decode workload timed",
                                      "ms_per_step": decode["ms_per_step"]}) + "\n")
+    granularity = None
+    if not args.no_granularity:
+        from mixture_experts_layer_renorm_amd.synth import GRANULARITY_PAIR
+        granularity = {}
+        for name in GRANULARITY_PAIR:
+            g, lay, _ = run_workload(name, args.steps, args.warmup, args.atomic_combine, hip)
+            del lay
+            torch.cuda.empty_cache()
+            granularity[name] = {
+                "T": g["T"], "D": g["D"], "E": g["E"], "K": g["K"], "F": g["F"], "U": g["U"],
+                "plan": g["plan"], "ms_per_step": g["ms_per_step"],
+                "tokens_per_s": g["tokens_per_s"], "layer_tflops": g["layer_tflops"],
+                "gate_up_tflops": g["gate_up"]["tflops"], "down_tflops": g["down"]["tflops"],
+                "gate_up_mfma_frac": g["gate_up"]["tflops"] / costmodel.MFMA_BF16_PEAK_TFLOPS,
+                "stage_ms": g["stage_ms"]}
+            sys.stderr.write(json.dumps({"progress": f"{name} timed",
+                                         "ms_per_step": g["ms_per_step"]}) + "\n")
     if args.copy_calibration:
         copy_calibration()
 
@@ -298,6 +318,7 @@ def main():
             "expert_weight_gbs": decode["expert_weight_gbs"],
             "expert_weight_hbm_frac": decode["expert_weight_gbs"] / costmodel.HBM_PEAK_GBS,
             "stage_ms": decode["stage_ms"]},
+        "granularity": granularity,
     }
     print(json.dumps(line))
 

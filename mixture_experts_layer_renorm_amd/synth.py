@@ -90,7 +90,18 @@ CONFIGS: Dict[str, LayerConfig] = {
         scoring=SIGMOID,
         description="DeepSeek-style sigmoid-affinity bf16 layer, T=16384 (D=4096, E=256, top-6, "
                     "F=2048, one ungated shared expert F=2048)"),
+    # granularity pair ("S23-J10" §4.1): halving E and K while doubling F keeps the routed
+    # parameters (3·E·D·F) and the per-token expert FLOPs (6·K·D·F) equal; only the GEMM shapes
+    # and the read pattern change.  D = 4096 is a stated choice (the page gives none).
+    "gran_e128": LayerConfig(
+        "gran_e128", T=4096, D=4096, E=128, K=8, F=1536,
+        description="granularity pair, fine: 128 experts x F=1536, top-8 (D=4096, T=4096)"),
+    "gran_e64": LayerConfig(
+        "gran_e64", T=4096, D=4096, E=64, K=4, F=3072,
+        description="granularity pair, coarse: 64 experts x F=3072, top-4 (D=4096, T=4096)"),
 }
+
+GRANULARITY_PAIR = ("gran_e128", "gran_e64")
 
 
 def hot_experts(cfg: LayerConfig):

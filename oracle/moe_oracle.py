@@ -51,7 +51,8 @@ SCORING_SIGMOID = "sigmoid"
 __all__ = [
     "SCORING_SOFTMAX", "SCORING_SIGMOID",
     "as_f64", "router_logits", "shared_gate", "selection_keys", "topk_select",
-    "routing_weights", "route", "dispatch", "silu", "sigmoid", "swiglu",
+    "routing_scores", "routing_weights", "topk_select_biased", "route", "update_select_bias",
+    "dispatch", "silu", "sigmoid", "swiglu",
     "moe_forward", "moe_forward_dense_masked",
     "expert_params", "expert_flops", "expert_read_bytes", "layer_flops",
 ]
@@ -127,6 +128,19 @@ def topk_select(logits: Any, K: int) -> np.ndarray:
     return order[:, :K].astype(np.int32)
 
 
+def routing_scores(logits: Any, scoring: str = SCORING_SOFTMAX) -> np.ndarray:
+    """Scores [T,E] (float64): softmax probabilities over all E experts ([MoE] §2), or the
+    per-expert sigmoid affinities ([Satori-1.6] §二 step 1, §四)."""
+    r = as_f64(logits)
+    if scoring == SCORING_SOFTMAX:
+        m = np.max(np.where(np.isnan(r), -np.inf, r), axis=1, keepdims=True)
+        e = np.exp(r - m)
+        return e / np.sum(e, axis=1, keepdims=True)
+    if scoring == SCORING_SIGMOID:
+        return sigmoid(r)
+    raise ValueError(f"unknown scoring {scoring!r}")
+
+
 def routing_weights(logits: Any, idx: Any, scoring: str = SCORING_SOFTMAX,
                     renormalize: bool = True) -> np.ndarray:
     """Weights α [T,K] (float64) of the selected experts.
@@ -135,27 +149,63 @@ def routing_weights(logits: Any, idx: Any, scoring: str = SCORING_SOFTMAX,
     sigmoid: s = sigmoid(r); α = s_e / Σ_{j∈I_t} s_j   ([Satori-1.6] §二 step 3, worked example).
     renormalize=False keeps p_e (or s_e) unnormalised, the plain top-k sum of [FFN-notes] §2.
     """
-    r = as_f64(logits)
+    score = routing_scores(logits, scoring)
     idx = np.asarray(idx, dtype=np.int64)
-    if scoring == SCORING_SOFTMAX:
-        m = np.max(np.where(np.isnan(r), -np.inf, r), axis=1, keepdims=True)
-        e = np.exp(r - m)
-        score = e / np.sum(e, axis=1, keepdims=True)
-    elif scoring == SCORING_SIGMOID:
-        score = sigmoid(r)
-    else:
-        raise ValueError(f"unknown scoring {scoring!r}")
     sel = np.take_along_axis(score, idx, axis=1)
     if renormalize:
         sel = sel / np.sum(sel, axis=1, keepdims=True)
     return sel
 
 
+def topk_select_biased(logits: Any, K: int, scoring: str, select_bias: Any) -> np.ndarray:
+    """Selection on s_e + b_e ([Satori-1.6] §三, DeepSeek-V3's auxiliary-loss-free balancing:
+    a per-expert bias enters only the top-k choice, never the gating weight).
+
+    s is the score of routing_scores (sigmoid affinity, or the softmax probability for a
+    softmax router -- the page states the rule for affinities; applying it to probabilities is
+    this oracle's reading).  Same total order as topk_select: key descending, id ascending;
+    a NaN key ranks as -inf.
+    """
+    keys = routing_scores(logits, scoring) + as_f64(select_bias)[None, :]
+    keys = selection_keys(keys)
+    T, E = keys.shape
+    if not 1 <= K <= E:
+        raise ValueError(f"need 1 <= K <= E, got K={K}, E={E}")
+    order = np.argsort(-keys, axis=1, kind="stable")
+    return order[:, :K].astype(np.int32)
+
+
 def route(logits: Any, K: int, scoring: str = SCORING_SOFTMAX,
-          renormalize: bool = True):
-    """(topk_idx [T,K] int32, topk_w [T,K] float64) from logits."""
-    idx = topk_select(logits, K)
+          renormalize: bool = True, select_bias: Optional[Any] = None):
+    """(topk_idx [T,K] int32, topk_w [T,K] float64) from logits.
+
+    With select_bias, the experts are chosen on score + bias and weighted with the unbiased
+    scores ([Satori-1.6] §三)."""
+    if select_bias is None:
+        idx = topk_select(logits, K)
+    else:
+        idx = topk_select_biased(logits, K, scoring, select_bias)
     return idx, routing_weights(logits, idx, scoring, renormalize)
+
+
+def update_select_bias(counts: Any, select_bias: Any, gamma: float) -> np.ndarray:
+    """One step of the bias feedback of [Satori-1.6] §三: an expert whose load is above the
+    mean load has its bias lowered by gamma, one below the mean raised by gamma, and one at the
+    mean keeps it.  The mean is Σ counts / E; the comparison is made exactly in integers
+    (counts_e · E against Σ counts).  Arithmetic in float32, the bias's storage type (one
+    rounding per expert), so the result is exact to compare."""
+    c = np.asarray(counts, dtype=np.int64)
+    b = np.asarray(select_bias, dtype=np.float32).copy()
+    E = c.shape[0]
+    total = int(c.sum())
+    g = np.float32(gamma)
+    for e in range(E):
+        d = int(c[e]) * E - total
+        if d > 0:
+            b[e] = np.float32(b[e] - g)
+        elif d < 0:
+            b[e] = np.float32(b[e] + g)
+    return b
 
 
 # ---------------------------------------------------------------------------------------------
@@ -219,7 +269,8 @@ def moe_forward(x: Any, w_router: Any, w_gate_up: Sequence[Any], w_down: Sequenc
                 logit_bias: Optional[Any] = None,
                 ws_gate_up: Optional[Any] = None, ws_down: Optional[Any] = None,
                 w_shared_gate: Optional[Any] = None,
-                logits: Optional[Any] = None) -> Dict[str, Any]:
+                logits: Optional[Any] = None,
+                select_bias: Optional[Any] = None) -> Dict[str, Any]:
     """Forward pass of one MoE layer, float64, without the residual.
 
     x [T,D]; w_router [E,D]; w_gate_up[e] [2F,D] and w_down[e] [D,F] are indexed one expert at a
@@ -228,6 +279,7 @@ def moe_forward(x: Any, w_router: Any, w_gate_up: Sequence[Any], w_down: Sequenc
     w_shared_gate: [1,D] sigmoid gate of the shared branch ([MoE] §4); None = ungated (g ≡ 1).
     logits: if given (e.g. fp32 logits exported by another implementation), routing is taken
     from them instead of being recomputed from x and w_router.
+    select_bias: [E] selection-only bias ([Satori-1.6] §三), or None.
 
     y_t = Σ_k α_{t,k} · E_{I_t[k]}(x_t) + g_t · E_s(x_t)
     """
@@ -238,7 +290,7 @@ def moe_forward(x: Any, w_router: Any, w_gate_up: Sequence[Any], w_down: Sequenc
     else:
         r = as_f64(logits)
     E = r.shape[1]
-    idx, alpha = route(r, K, scoring, renormalize)
+    idx, alpha = route(r, K, scoring, renormalize, select_bias)
     d = dispatch(idx, E)
     counts, offsets, perm, inv_perm = d["counts"], d["offsets"], d["perm"], d["inv_perm"]
 

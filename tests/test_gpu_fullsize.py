@@ -28,7 +28,7 @@ DEV = "cuda"
 
 # workload -> number of sampled tokens for the output check
 WORKLOADS = {"a3b_decode": 64, "a3b_prefill": 24, "skew": 24, "skew_conc": 24, "a17b": 12,
-             "ds_sigmoid": 10}
+             "ds_sigmoid": 10, "gran_e128": 12, "gran_e64": 12}
 
 
 @pytest.fixture(scope="module", params=list(WORKLOADS))
