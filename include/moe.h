@@ -94,13 +94,18 @@ typedef struct {
   const void *ws_gate_up;  /* [2*F_shared, D]  (shared expert; NULL iff F_shared == 0)     */
   const void *ws_down;     /* [D, F_shared]                                                */
   const void *ws_gate;     /* [1, D] shared-expert gate projection (required iff gated)    */
+  const float *select_bias;/* [E] fp32 selection-only bias, or NULL ("1.6 ..." §三,
+                              DeepSeek-V3's auxiliary-loss-free balancing): experts are
+                              chosen on score + bias and weighted with the unbiased score,
+                              where score = softmax probability or sigmoid affinity        */
 } moe_weights;
 
 /* Routing tensors.  Which fields are inputs and which are outputs depends on the call. */
 typedef struct {
   float *logits;           /* [T, E] fp32 router logits (bias included)                    */
-  int32_t *topk_idx;       /* [T, K] selected experts, slots in descending logit order,
-                              ties to the lower expert id; ids outside [0,E) are skipped
+  int32_t *topk_idx;       /* [T, K] selected experts, slots in descending key order (the
+                              logit; with a select_bias, score + bias), ties to the lower
+                              expert id; ids outside [0,E) are skipped
                               by dispatch and combine (sentinels)                          */
   float *topk_w;           /* [T, K] fp32 weights a_t,e                                    */
   int32_t *expert_counts;  /* [E]   t_e = assignments routed to expert e                   */
@@ -121,15 +126,26 @@ int moe_workspace_size(const moe_problem *p, size_t *bytes);
  * Out: r->topk_idx, r->topk_w (required); r->logits (optional, [T,E] fp32);
  *      r->shared_gate (optional, only written for a gated shared expert).
  * Logits are fp32 MFMA accumulations of the dtype inputs; selection compares these fp32
- * values exactly (a NaN logit ranks as -inf; -0 equals +0). */
+ * values exactly (a NaN logit ranks as -inf; -0 equals +0).  With w->select_bias the key is
+ * the fp32 score + bias instead (the same total order on that key). */
 int moe_route(const moe_problem *p, const void *x, const moe_weights *w, moe_routing *r,
               void *workspace, size_t workspace_bytes, moe_stream_t stream);
 
 /* Stage 1 from given logits: top-K selection and weights only.
- * In: logits [T,E] fp32 (bias, if any, already included).  Out: r->topk_idx, r->topk_w.
+ * In: logits [T,E] fp32 (logit bias, if any, already included); select_bias [E] fp32 or
+ * NULL (as moe_weights.select_bias).  Out: r->topk_idx, r->topk_w.
  * No workspace.  Used to check selection bit-exactly on shared logits. */
-int moe_route_logits(const moe_problem *p, const float *logits, moe_routing *r,
-                     moe_stream_t stream);
+int moe_route_logits(const moe_problem *p, const float *logits, const float *select_bias,
+                     moe_routing *r, moe_stream_t stream);
+
+/* One step of the selection-bias feedback ("1.6 ..." §三): with the loads t_e of a dispatch
+ * (expert_counts [E] int32) and their mean m = sum(t) / E, select_bias[e] (fp32 [E], updated
+ * in place) is lowered by gamma if t_e > m, raised by gamma if t_e < m, kept if t_e = m.
+ * The comparison is exact (t_e * E against sum(t) in 64-bit integers); each update is one
+ * fp32 add.  One work-group; no workspace.  MOE_ERR_INVALID_ARG for NULL or unaligned
+ * pointers. */
+int moe_update_select_bias(const moe_problem *p, const int32_t *expert_counts,
+                           float *select_bias, float gamma, moe_stream_t stream);
 
 /* Stage 2, dispatch ("MoE" §3.2: gather the tokens of each hit expert).
  * In: r->topk_idx.  Out: r->expert_counts, r->expert_offsets, r->perm, r->inv_perm (required).

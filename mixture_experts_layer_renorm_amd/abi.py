@@ -32,7 +32,7 @@ MOE_FLAG_NO_RENORM = 2
 
 SYMBOLS = ("moe_workspace_size", "moe_route", "moe_route_logits", "moe_dispatch",
            "moe_experts", "moe_combine", "moe_forward", "moe_forward_timed",
-           "moe_status_string", "moe_last_error", "moe_describe_plan")
+           "moe_status_string", "moe_last_error", "moe_describe_plan", "moe_update_select_bias")
 MOE_STAGE_NAMES = ("router", "topk", "dispatch", "gate_up", "shared", "down", "final")
 MOE_STAGE_COUNT = len(MOE_STAGE_NAMES)
 MOE_STAGE_GATE_UP = MOE_STAGE_NAMES.index("gate_up")
@@ -50,7 +50,8 @@ class moe_problem(ctypes.Structure):
 
 
 _WEIGHT_FIELDS = ("w_router", "logit_bias", "w_gate_up", "w_down", "ws_gate_up", "ws_down",
-                  "ws_gate")
+                  "ws_gate", "select_bias")
+_FP32_WEIGHTS = ("logit_bias", "select_bias")
 _ROUTING_FIELDS = ("logits", "topk_idx", "topk_w", "expert_counts", "expert_offsets", "perm",
                    "inv_perm", "shared_gate")
 
@@ -85,7 +86,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     prob = P(moe_problem)
     lib.moe_workspace_size.argtypes = [prob, P(ctypes.c_size_t)]
     lib.moe_route.argtypes = [prob, vp, P(moe_weights), P(moe_routing), vp, sz, vp]
-    lib.moe_route_logits.argtypes = [prob, vp, P(moe_routing), vp]
+    lib.moe_route_logits.argtypes = [prob, vp, vp, P(moe_routing), vp]
+    lib.moe_update_select_bias.argtypes = [prob, vp, vp, ctypes.c_float, vp]
     lib.moe_dispatch.argtypes = [prob, vp, P(moe_routing), vp, vp, sz, vp]
     lib.moe_experts.argtypes = [prob, vp, vp, P(moe_weights), P(moe_routing), vp, vp, vp, sz, vp]
     lib.moe_combine.argtypes = [prob, vp, P(moe_routing), vp, vp, vp]
@@ -93,7 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward_timed.argtypes = [prob, vp, P(moe_weights), P(moe_routing), vp, vp, sz, vp,
                                       P(ctypes.c_void_p)]
     for n in ("moe_workspace_size", "moe_route", "moe_route_logits", "moe_dispatch",
-              "moe_experts", "moe_combine", "moe_forward", "moe_forward_timed"):
+              "moe_experts", "moe_combine", "moe_forward", "moe_forward_timed",
+              "moe_update_select_bias"):
         getattr(lib, n).restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -151,7 +154,7 @@ def _weights(p: moe_problem, w: Dict[str, Optional[torch.Tensor]]) -> moe_weight
     out = moe_weights()
     for n in _WEIGHT_FIELDS:
         t = w.get(n)
-        setattr(out, n, _ptr(t, n, torch.float32 if n == "logit_bias" else dt))
+        setattr(out, n, _ptr(t, n, torch.float32 if n in _FP32_WEIGHTS else dt))
     return out
 
 
@@ -210,11 +213,22 @@ def moe_route(p: moe_problem, x: torch.Tensor, weights: Dict, routing: Dict,
                          ctypes.byref(r), wp, wb, _stream(stream)))
 
 
-def moe_route_logits(p: moe_problem, logits: torch.Tensor, routing: Dict, stream=None) -> None:
+def moe_route_logits(p: moe_problem, logits: torch.Tensor, routing: Dict, stream=None,
+                     select_bias: Optional[torch.Tensor] = None) -> None:
     lib = load_library()
     r = _routing(routing)
     _check(lib.moe_route_logits(ctypes.byref(p), _ptr(logits, "logits", torch.float32),
+                                _ptr(select_bias, "select_bias", torch.float32),
                                 ctypes.byref(r), _stream(stream)))
+
+
+def moe_update_select_bias(p: moe_problem, expert_counts: torch.Tensor,
+                           select_bias: torch.Tensor, gamma: float, stream=None) -> None:
+    lib = load_library()
+    _check(lib.moe_update_select_bias(ctypes.byref(p),
+                                      _ptr(expert_counts, "expert_counts", torch.int32),
+                                      _ptr(select_bias, "select_bias", torch.float32),
+                                      ctypes.c_float(gamma), _stream(stream)))
 
 
 def moe_dispatch(p: moe_problem, x: Optional[torch.Tensor], routing: Dict,

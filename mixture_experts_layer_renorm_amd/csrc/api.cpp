@@ -356,6 +356,7 @@ int check_weights(const moe_problem* p, const moe_weights* w, bool router, bool 
   if (router) {
     MOE_CHECK_PTR(w->w_router, "w_router");
     MOE_CHECK_OPT(w->logit_bias, "logit_bias");
+    MOE_CHECK_OPT(w->select_bias, "select_bias");
     if (gated(p)) MOE_CHECK_PTR(w->ws_gate, "ws_gate");
   }
   if (experts) {
@@ -449,17 +450,19 @@ int moe_route(const moe_problem* p, const void* x, const moe_weights* w, moe_rou
   ta.w = r->topk_w;
   ta.logits_out = r->logits;
   ta.gate_out = want_gate ? r->shared_gate : nullptr;
+  ta.sel_bias = w->select_bias;
   MOE_HIP_TRY(moe::launch_topk(ta, s), "top-K launch");
   return MOE_OK;
 }
 
-int moe_route_logits(const moe_problem* p, const float* logits, moe_routing* r,
-                     moe_stream_t stream) {
+int moe_route_logits(const moe_problem* p, const float* logits, const float* select_bias,
+                     moe_routing* r, moe_stream_t stream) {
   g_last_error.clear();
   int st = check_problem(p);
   if (st) return st;
   if (p->T == 0) return MOE_OK;
   MOE_CHECK_PTR(logits, "logits");
+  MOE_CHECK_OPT(select_bias, "select_bias");
   if (!r) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
   MOE_CHECK_PTR(r->topk_idx, "topk_idx");
   MOE_CHECK_PTR(r->topk_w, "topk_w");
@@ -474,7 +477,21 @@ int moe_route_logits(const moe_problem* p, const float* logits, moe_routing* r,
   ta.renorm = !(p->flags & MOE_FLAG_NO_RENORM);
   ta.idx = r->topk_idx;
   ta.w = r->topk_w;
+  ta.sel_bias = select_bias;
   MOE_HIP_TRY(moe::launch_topk(ta, (hipStream_t)stream), "top-K launch");
+  return MOE_OK;
+}
+
+int moe_update_select_bias(const moe_problem* p, const int32_t* expert_counts,
+                           float* select_bias, float gamma, moe_stream_t stream) {
+  g_last_error.clear();
+  int st = check_problem(p);
+  if (st) return st;
+  MOE_CHECK_PTR(expert_counts, "expert_counts");
+  MOE_CHECK_PTR(select_bias, "select_bias");
+  MOE_HIP_TRY(moe::launch_update_select_bias(expert_counts, p->E, select_bias, gamma,
+                                             (hipStream_t)stream),
+              "bias update launch");
   return MOE_OK;
 }
 
@@ -625,6 +642,7 @@ int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_
   ta.w = r.topk_w;
   ta.logits_out = r.logits;  // only if the caller asked for them
   ta.gate_out = g ? r.shared_gate : nullptr;
+  ta.sel_bias = w->select_bias;
   MOE_HIP_TRY(moe::launch_topk(ta, s), "top-K launch");
   // 2. dispatch + tile map
   const GroupedPlan plan = grouped_plan(p);

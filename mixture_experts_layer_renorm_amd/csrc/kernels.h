@@ -98,7 +98,10 @@ struct TopkArgs {
   const float* gate_src;
   int64_t gate_ld;
   float* gate_out;
+  const float* sel_bias;  // [E] or null: choose on score + bias, weight with the score
 };
+hipError_t launch_update_select_bias(const int32_t* counts, int E, float* bias, float gamma,
+                                     hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 
 // Router logits from bf16 x [T, D] and W_r [E, D] (+ gate row [D]): K split into ks slices,

@@ -37,6 +37,12 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   return v;
 }
 
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
@@ -81,7 +87,39 @@ __global__ void __launch_bounds__(256) topk_kernel(const TopkArgs a) {
                    : 0ull;  // below every real key
   }
 
-  // Slot k (k < K <= 64) is kept by lane k: its logit and expert id.
+  // Selection-only bias: the key becomes score + bias (score = softmax probability over all
+  // E experts, or the sigmoid affinity); the weights below use the unbiased score.
+  float sc[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) sc[j] = 0.0f;
+  if (a.sel_bias) {
+    if (a.scoring == 0) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+        if (lane + 64 * j < E) m = fmaxf(m, val[j]);
+      m = wave_max_f(m);
+      float part = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+        if (lane + 64 * j < E) part += expf(val[j] - m);
+      const float sum = wave_sum(part);
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) sc[j] = expf(val[j] - m) / sum;
+    } else {
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) sc[j] = 1.0f / (1.0f + expf(-val[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E)
+        key[j] = ((unsigned long long)order_key(sc[j] + a.sel_bias[e]) << 32) |
+                 (0xFFFFFFFFu - (uint32_t)e);
+    }
+  }
+
+  // Slot k (k < K <= 64) is kept by lane k: its logit (or, with a bias, its score) and id.
   float top = 0.0f, my_val = 0.0f;
   int my_id = 0;
   for (int k = 0; k < K; ++k) {
@@ -97,25 +135,35 @@ __global__ void __launch_bounds__(256) topk_kernel(const TopkArgs a) {
       for (int j = 0; j < NPL; ++j)
         if (j == (int)(e >> 6)) key[j] = 0ull;
     }
+    float mv = v;
+    if (a.sel_bias) {  // the selected expert's unbiased score, from the lane that holds it
+      float own = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+        if (j == (int)(e >> 6)) own = sc[j];
+      mv = __shfl(own, (int)(e & 63u), 64);
+    }
     if (lane == k) {
-      my_val = v;
+      my_val = mv;
       my_id = (int)e;
     }
   }
 
-  float s = 0.0f;
-  if (lane < K) s = a.scoring == 0 ? expf(my_val - top) : 1.0f / (1.0f + expf(-my_val));
-  float denom;
-  if (a.renorm) {
-    denom = wave_sum(s);
-  } else if (a.scoring == 0) {
-    float part = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j)
-      if (lane + 64 * j < E) part += expf(val[j] - top);
-    denom = wave_sum(part);
+  float s = 0.0f, denom = 1.0f;
+  if (a.sel_bias) {
+    if (lane < K) s = my_val;  // the slot's unbiased score
+    if (a.renorm) denom = wave_sum(s);
   } else {
-    denom = 1.0f;
+    if (lane < K) s = a.scoring == 0 ? expf(my_val - top) : 1.0f / (1.0f + expf(-my_val));
+    if (a.renorm) {
+      denom = wave_sum(s);
+    } else if (a.scoring == 0) {
+      float part = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+        if (lane + 64 * j < E) part += expf(val[j] - top);
+      denom = wave_sum(part);
+    }
   }
   if (lane < K) {
     a.idx[t * K + lane] = my_id;
@@ -198,7 +246,34 @@ __global__ void __launch_bounds__(256) router_kernel(const __bf16* __restrict__ 
   }
 }
 
+// Selection-bias feedback: one work-group; the load total in 64-bit integers, then one fp32
+// add per expert.
+__global__ void __launch_bounds__(1024) update_bias_kernel(const int32_t* __restrict__ counts,
+                                                           int E, float* __restrict__ bias,
+                                                           float gamma) {
+  __shared__ long long part[16];
+  long long sum = 0;
+  for (int e = threadIdx.x; e < E; e += 1024) sum += counts[e];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = sum;
+  __syncthreads();
+  long long total = 0;
+  for (int w = 0; w < 16; ++w) total += part[w];
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    const long long d = (long long)counts[e] * E - total;
+    if (d > 0) bias[e] = bias[e] - gamma;
+    else if (d < 0) bias[e] = bias[e] + gamma;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_update_select_bias(const int32_t* counts, int E, float* bias, float gamma,
+                                     hipStream_t stream) {
+  hipLaunchKernelGGL(update_bias_kernel, dim3(1), dim3(1024), 0, stream, counts, E, bias, gamma);
+  return hipGetLastError();
+}
 
 int router_kslices(int64_t T, int D, int E, int gated) {
   const int64_t blocks = ((T + 15) / 16) * ((E + gated + 63) / 64);

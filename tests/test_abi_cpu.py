@@ -156,8 +156,16 @@ def test_invalid_calls_fail_before_launch(lib):
                          need, None) == abi.MOE_ERR_INVALID_ARG
     pk = _prob(K=9)
     r2 = abi.moe_routing(topk_idx=ALIGNED, topk_w=ALIGNED)
-    assert lib.moe_route_logits(ctypes.byref(pk), ALIGNED, ctypes.byref(r2),
+    assert lib.moe_route_logits(ctypes.byref(pk), ALIGNED, None, ctypes.byref(r2),
                                 None) == abi.MOE_ERR_INVALID_ARG
+    # unaligned select_bias; bias update without counts / with an unaligned bias
+    r3 = abi.moe_routing(topk_idx=ALIGNED, topk_w=ALIGNED)
+    assert lib.moe_route_logits(ctypes.byref(p), ALIGNED, ALIGNED + 4, ctypes.byref(r3),
+                                None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_update_select_bias(ctypes.byref(p), None, ALIGNED, 0.01,
+                                      None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_update_select_bias(ctypes.byref(p), ALIGNED, ALIGNED + 4, 0.01,
+                                      None) == abi.MOE_ERR_INVALID_ARG
     # dispatch / experts / combine: missing routing tensors
     assert lib.moe_dispatch(ctypes.byref(p), None, ctypes.byref(r), None, ALIGNED, need,
                             None) == abi.MOE_ERR_INVALID_ARG

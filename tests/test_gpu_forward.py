@@ -177,3 +177,26 @@ def test_every_grouped_tile_shape_matches_oracle(name, tile, monkeypatch):
         _check_routing(cfg, r, ref)
         err = rel_max_err(out32, ref["out"])
         assert err <= _tol(cfg), f"{name}/{tile}/atomic={atomic}: max|err|/RMS = {err:.3e}"
+
+
+@pytest.mark.parametrize("name", ["ds_sigmoid_E16", "a3b_E16", "a3b_decode"])
+def test_forward_with_select_bias(name):
+    """moe_forward with a selection-only bias: routing bit-exact against the oracle fed the
+    GPU's logits and the same bias, output within the layer's tolerance."""
+    cfg, layer, T = _case(name)
+    g = torch.Generator(device="cpu").manual_seed(77)
+    scale = 0.05 if cfg.scoring == "sigmoid" else 2.0 / cfg.E
+    bias = (torch.randn(cfg.E, generator=g) * scale).to(torch.float32)
+    p = problem_for(cfg, T=T, out_dtype=torch.float32)
+    r = abi.alloc_routing(p, DEV)
+    out = torch.empty((T, cfg.D), dtype=torch.float32, device=DEV)
+    w = weights_for(layer)
+    w["select_bias"] = bias.to(DEV)
+    abi.moe_forward(p, layer["x"], w, r, out, abi.alloc_workspace(p, DEV))
+    torch.cuda.synchronize()
+    args, kw = oracle_args(cfg, layer)
+    ref = O.moe_forward(*args, logits=f64(r["logits"]), select_bias=f64(bias), **kw)
+    _check_routing(cfg, r, ref)
+    plain = O.topk_select(f64(r["logits"]), cfg.K)
+    assert np.any(np.sort(ref["topk_idx"], 1) != np.sort(plain, 1))  # the bias mattered
+    assert rel_max_err(out, ref["out"]) <= _tol(cfg)

@@ -144,3 +144,64 @@ def test_router_gemm_and_topk(name, T):
         want_g = O.shared_gate(X, Ws)
         gbound = 0.25 * _fp32_logit_bound(X, Ws, X @ Ws.T)[:, 0] + 1e-7
         assert np.all(np.abs(f64(r["shared_gate"]) - want_g) <= gbound)
+
+
+# ---- selection-only bias ("1.6 ..." §三): choose on score + bias, weight with the score ----
+
+def _near_tie_ok(keys64, got_idx, want_idx, K, delta):
+    """Tokens whose GPU and oracle choices differ must have the oracle's K-th and (K+1)-th
+    keys within delta (the fp32 score's rounding against the float64 one)."""
+    differ = np.nonzero(np.any(np.sort(got_idx, 1) != np.sort(want_idx, 1), axis=1))[0]
+    for t in differ:
+        srt = np.sort(keys64[t])[::-1]
+        assert srt[K - 1] - srt[K] <= delta, (t, srt[K - 1] - srt[K])
+    return differ
+
+
+@pytest.mark.parametrize("E,K", [(8, 2), (256, 8), (256, 6), (64, 64), (130, 3), (1024, 16)])
+@pytest.mark.parametrize("scoring", ["softmax", "sigmoid"])
+@pytest.mark.parametrize("renormalize", [True, False])
+def test_topk_select_bias(E, K, scoring, renormalize):
+    g = torch.Generator().manual_seed(E * 7 + K)
+    T = 700
+    logits = torch.randn((T, E), generator=g) * 1.5
+    # a bias comparable to the spread of the scores, so it really moves the choice
+    scale = 0.05 if scoring == "sigmoid" else 2.0 / E
+    bias = (torch.randn(E, generator=g) * scale).to(torch.float32)
+    p = abi.make_problem(T=T, D=64, E=E, K=K, F=64, scoring=scoring, renormalize=renormalize)
+    r = {"topk_idx": torch.empty((T, K), dtype=torch.int32, device=DEV),
+         "topk_w": torch.empty((T, K), dtype=torch.float32, device=DEV)}
+    abi.moe_route_logits(p, logits.to(DEV), r, select_bias=bias.to(DEV))
+    torch.cuda.synchronize()
+    L, b = f64(logits), f64(bias)
+    got = i64(r["topk_idx"])
+    want = O.topk_select_biased(L, K, scoring, b)
+    if K < E:
+        keys = O.routing_scores(L, scoring) + b[None, :]
+        differ = _near_tie_ok(keys, got, want, K, delta=1e-6)
+        assert len(differ) <= max(1, T // 100)
+    else:
+        differ = np.array([], dtype=np.int64)
+    same = np.setdiff1d(np.arange(T), differ)
+    np.testing.assert_array_equal(got[same], want[same])
+    want_w = O.routing_weights(L, want, scoring, renormalize)
+    np.testing.assert_allclose(f64(r["topk_w"])[same], want_w[same], rtol=0, atol=TOL_ROUTING_W)
+    # the bias moved the choice of many tokens away from the unbiased router's
+    if K < E:
+        assert np.mean(np.any(np.sort(got, 1) != np.sort(O.topk_select(L, K), 1), axis=1)) > 0.05
+
+
+@pytest.mark.parametrize("E", [1, 7, 256, 1024])
+def test_update_select_bias_bit_exact(E):
+    g = torch.Generator().manual_seed(E)
+    counts = torch.randint(0, 40, (E,), generator=g, dtype=torch.int32)
+    if E >= 7:
+        counts[3] = 0
+        counts[:E // 2] = int(counts.sum()) // E  # some at the integer mean (maybe not exact)
+    bias = (torch.randn(E, generator=g) * 0.1).to(torch.float32)
+    p = abi.make_problem(T=1, D=64, E=E, K=1, F=64)
+    b_dev = bias.to(DEV)
+    abi.moe_update_select_bias(p, counts.to(DEV), b_dev, 1e-3)
+    torch.cuda.synchronize()
+    want = O.update_select_bias(counts.numpy(), bias.numpy(), 1e-3)
+    assert np.array_equal(b_dev.cpu().numpy().view(np.uint32), want.view(np.uint32))
