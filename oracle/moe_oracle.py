@@ -52,6 +52,7 @@ __all__ = [
     "SCORING_SOFTMAX", "SCORING_SIGMOID",
     "as_f64", "router_logits", "shared_gate", "selection_keys", "topk_select",
     "routing_scores", "routing_weights", "topk_select_biased", "route", "update_select_bias",
+    "router_stats",
     "dispatch", "silu", "sigmoid", "swiglu",
     "moe_forward", "moe_forward_dense_masked",
     "expert_params", "expert_flops", "expert_read_bytes", "layer_flops",
@@ -206,6 +207,43 @@ def update_select_bias(counts: Any, select_bias: Any, gamma: float) -> np.ndarra
         elif d < 0:
             b[e] = np.float32(b[e] + g)
     return b
+
+
+def router_stats(logits: Any, counts: Any, scoring: str = SCORING_SOFTMAX) -> Dict[str, Any]:
+    """Load-balance and stability statistics of one routed batch.
+
+    f[i]  = t_i / Σ_j t_j, the fraction of the batch's dispatched assignments on expert i
+            (the hard counts of [Satori-1.6] §三; Σ f = 1).
+    P[i]  = mean over tokens of the router probability of expert i: the softmax probability
+            ([Satori-1.6] §三); for a sigmoid router, the affinities normalised over all E
+            experts of the token (this oracle's reading, so that Σ P = 1 as the page requires).
+    aux   = N · Σ_i f_i P_i, the auxiliary balance loss before its weight α ([Satori-1.6] §三;
+            1 when f and P are uniform, N when both sit on one expert).
+    z     = mean over tokens of (log Σ_j exp r_tj)², the router z-loss before its weight
+            ([Satori-1.6] §六).
+    cv    = std(t) / mean(t) over the E experts, population standard deviation (the load
+            coefficient of variation of the routing visualisation on the "Qwen3.6-27B" page,
+            §五), and max_over_mean = max(t) / mean(t).
+    """
+    r = as_f64(logits)
+    t = np.asarray(counts, dtype=np.float64)
+    T, E = r.shape
+    total = t.sum()
+    f = t / total if total > 0 else np.zeros(E)
+    m = np.max(r, axis=1, keepdims=True)
+    lse = m[:, 0] + np.log(np.sum(np.exp(r - m), axis=1))
+    if scoring == SCORING_SOFTMAX:
+        prob = np.exp(r - lse[:, None])
+    elif scoring == SCORING_SIGMOID:
+        s = sigmoid(r)
+        prob = s / np.sum(s, axis=1, keepdims=True)
+    else:
+        raise ValueError(f"unknown scoring {scoring!r}")
+    P = prob.mean(axis=0)
+    mean = total / E
+    return {"f": f, "P": P, "aux": float(E * np.sum(f * P)), "z": float(np.mean(lse ** 2)),
+            "cv": float(t.std() / mean) if mean > 0 else 0.0,
+            "max_over_mean": float(t.max() / mean) if mean > 0 else 0.0}
 
 
 # ---------------------------------------------------------------------------------------------

@@ -124,6 +124,59 @@ def test_update_select_bias_feedback():
     np.testing.assert_array_equal(O.update_select_bias([4, 4, 4], b[:3], 0.5), b[:3])
 
 
+def test_router_stats_balance_extremes():
+    """[Satori-1.6] §三: Σ f_i P_i is smallest, 1/N, when f and P are uniform, so N·Σ f P = 1;
+    with every token's routing and probability on one expert it is N."""
+    T, E, K = 40, 8, 2
+    st = O.router_stats(np.zeros((T, E)), np.full(E, T * K // E))
+    np.testing.assert_allclose(st["f"], 1 / E, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(st["P"], 1 / E, rtol=0, atol=1e-15)
+    assert abs(st["aux"] - 1.0) < 1e-14 and st["cv"] == 0.0 and st["max_over_mean"] == 1.0
+    r = np.full((T, E), -1e4)
+    r[:, 3] = 0.0
+    counts = np.zeros(E, dtype=np.int64)
+    counts[3] = T
+    st = O.router_stats(r, counts)
+    assert abs(st["aux"] - E) < 1e-9
+    # one expert holds everything: std = mean·sqrt(E-1), max = E·mean
+    assert abs(st["cv"] - np.sqrt(E - 1)) < 1e-12 and st["max_over_mean"] == E
+
+
+def test_router_stats_z_loss_and_cv_by_hand():
+    """z-loss ([Satori-1.6] §六) of constant logits c over E experts is (c + log E)²; the
+    loads 10, 2, 5, 3 have mean 5 and population std sqrt(9.5)."""
+    E = 6
+    st = O.router_stats(np.full((3, E), 2.5), [10, 2, 5, 3, 0, 10])
+    assert abs(st["z"] - (2.5 + np.log(E)) ** 2) < 1e-12
+    st = O.router_stats(np.zeros((2, 4)), [10, 2, 5, 3])
+    assert abs(st["cv"] - np.sqrt(9.5) / 5) < 1e-15
+    assert abs(st["max_over_mean"] - 2.0) < 1e-15
+    np.testing.assert_allclose(st["f"], [0.5, 0.1, 0.25, 0.15], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("scoring", [O.SCORING_SOFTMAX, O.SCORING_SIGMOID])
+def test_router_stats_are_distributions(scoring):
+    rng = np.random.default_rng(41)
+    T, E, K = 64, 16, 4
+    r = rng.standard_normal((T, E)) * 3
+    idx = O.topk_select(r, K)
+    counts = O.dispatch(idx, E)["counts"]
+    st = O.router_stats(r, counts, scoring)
+    assert abs(st["f"].sum() - 1) < 1e-14 and abs(st["P"].sum() - 1) < 1e-14
+    assert np.all(st["P"] > 0)
+    # aux is N times an inner product of two distributions: between 0 and N
+    assert 0 < st["aux"] <= E
+    # brute force of the softmax mean probability, token by token
+    if scoring == O.SCORING_SOFTMAX:
+        P = np.zeros(E)
+        for t in range(T):
+            ex = [math.exp(v) for v in r[t]]
+            P += np.array(ex) / sum(ex)
+        np.testing.assert_allclose(st["P"], P / T, rtol=1e-13)
+        z = np.mean([math.log(sum(math.exp(v) for v in r[t])) ** 2 for t in range(T)])
+        assert abs(st["z"] - z) < 1e-12 * z
+
+
 def test_worked_example_output():
     """y = u + g2·FFN2(u) + g5·FFN5(u); the layer output is everything but the residual u."""
     g = _golden("worked_example_e5_k2.json")
