@@ -138,6 +138,19 @@ int moe_route(const moe_problem *p, const void *x, const moe_weights *w, moe_rou
 int moe_route_logits(const moe_problem *p, const float *logits, const float *select_bias,
                      moe_routing *r, moe_stream_t stream);
 
+/* Router statistics of one routed batch ("1.6 ..." §三 auxiliary balance loss, §六 router
+ * z-loss).  In: logits [T,E] fp32 (e.g. r->logits of moe_route / moe_forward, bias included),
+ * expert_counts [E] int32 (the dispatch histogram).  Out: stats [2E + 4] fp32:
+ *   stats[e]       f_e = t_e / sum(t), the fraction of dispatched assignments on expert e
+ *   stats[E + e]   P_e = mean over tokens of the router probability of expert e (softmax; for a
+ *                  sigmoid router the affinities normalised over the token's E experts)
+ *   stats[2E]      E * sum_e f_e P_e (the balance loss before its weight; 1 when uniform)
+ *   stats[2E + 1]  mean over tokens of (log sum_e exp r_te)^2 (the z-loss before its weight)
+ *   stats[2E + 2]  population std / mean of the loads t_e;  stats[2E + 3]  max t_e / mean t_e
+ * Deterministic (fixed-order reductions, no atomics).  Uses the workspace.  T = 0: no-op. */
+int moe_router_stats(const moe_problem *p, const float *logits, const int32_t *expert_counts,
+                     float *stats, void *workspace, size_t workspace_bytes, moe_stream_t stream);
+
 /* One step of the selection-bias feedback ("1.6 ..." §三): with the loads t_e of a dispatch
  * (expert_counts [E] int32) and their mean m = sum(t) / E, select_bias[e] (fp32 [E], updated
  * in place) is lowered by gamma if t_e > m, raised by gamma if t_e < m, kept if t_e = m.

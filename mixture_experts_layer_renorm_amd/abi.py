@@ -32,7 +32,8 @@ MOE_FLAG_NO_RENORM = 2
 
 SYMBOLS = ("moe_workspace_size", "moe_route", "moe_route_logits", "moe_dispatch",
            "moe_experts", "moe_combine", "moe_forward", "moe_forward_timed",
-           "moe_status_string", "moe_last_error", "moe_describe_plan", "moe_update_select_bias")
+           "moe_status_string", "moe_last_error", "moe_describe_plan", "moe_update_select_bias",
+           "moe_router_stats")
 MOE_STAGE_NAMES = ("router", "topk", "dispatch", "gate_up", "shared", "down", "final")
 MOE_STAGE_COUNT = len(MOE_STAGE_NAMES)
 MOE_STAGE_GATE_UP = MOE_STAGE_NAMES.index("gate_up")
@@ -88,6 +89,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_route.argtypes = [prob, vp, P(moe_weights), P(moe_routing), vp, sz, vp]
     lib.moe_route_logits.argtypes = [prob, vp, vp, P(moe_routing), vp]
     lib.moe_update_select_bias.argtypes = [prob, vp, vp, ctypes.c_float, vp]
+    lib.moe_router_stats.argtypes = [prob, vp, vp, vp, vp, sz, vp]
     lib.moe_dispatch.argtypes = [prob, vp, P(moe_routing), vp, vp, sz, vp]
     lib.moe_experts.argtypes = [prob, vp, vp, P(moe_weights), P(moe_routing), vp, vp, vp, sz, vp]
     lib.moe_combine.argtypes = [prob, vp, P(moe_routing), vp, vp, vp]
@@ -96,7 +98,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       P(ctypes.c_void_p)]
     for n in ("moe_workspace_size", "moe_route", "moe_route_logits", "moe_dispatch",
               "moe_experts", "moe_combine", "moe_forward", "moe_forward_timed",
-              "moe_update_select_bias"):
+              "moe_update_select_bias", "moe_router_stats"):
         getattr(lib, n).restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -220,6 +222,21 @@ def moe_route_logits(p: moe_problem, logits: torch.Tensor, routing: Dict, stream
     _check(lib.moe_route_logits(ctypes.byref(p), _ptr(logits, "logits", torch.float32),
                                 _ptr(select_bias, "select_bias", torch.float32),
                                 ctypes.byref(r), _stream(stream)))
+
+
+def moe_router_stats(p: moe_problem, logits: torch.Tensor, expert_counts: torch.Tensor,
+                     workspace: torch.Tensor, stream=None) -> Dict[str, torch.Tensor]:
+    """Router statistics; returns f [E], P [E] and the scalars aux, z, cv, max_over_mean as
+    0-d fp32 device tensors (views of one [2E + 4] buffer)."""
+    lib = load_library()
+    E = p.E
+    out = torch.empty(2 * E + 4, dtype=torch.float32, device=logits.device)
+    wp, wb = _ws(workspace)
+    _check(lib.moe_router_stats(ctypes.byref(p), _ptr(logits, "logits", torch.float32),
+                                _ptr(expert_counts, "expert_counts", torch.int32),
+                                _ptr(out, "stats", torch.float32), wp, wb, _stream(stream)))
+    return {"f": out[:E], "P": out[E:2 * E], "aux": out[2 * E], "z": out[2 * E + 1],
+            "cv": out[2 * E + 2], "max_over_mean": out[2 * E + 3]}
 
 
 def moe_update_select_bias(p: moe_problem, expert_counts: torch.Tensor,

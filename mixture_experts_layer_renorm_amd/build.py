@@ -19,7 +19,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["gemm.hip", "gemm_stream.hip", "gemm_mfma.hip", "route.hip", "dispatch.hip", "combine.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "gemm_stream.hip", "gemm_mfma.hip", "route.hip", "dispatch.hip", "combine.hip",
+           "stats.hip", "api.cpp"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",

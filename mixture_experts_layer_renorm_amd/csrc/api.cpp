@@ -140,7 +140,7 @@ moe::TileCfg dense_cfg(int64_t M, int64_t N, int dtype = MOE_DTYPE_F32) {
 // Workspace layout: every region 256-byte aligned.
 struct Layout {
   size_t logits, gate_logit, gate, topk_idx, topk_w, counts, offsets, perm, inv_perm, seg_counts,
-      tiles, tile_count, H, Hs, acc, y_perm, y_shared, total;
+      tiles, tile_count, H, Hs, acc, y_perm, y_shared, stats, total;
   int64_t max_mtiles;
 };
 
@@ -183,6 +183,7 @@ Layout layout(const moe_problem* p) {
     L.y_perm = take((size_t)A * D * 4);
     L.y_shared = take(has_shared(p) ? (size_t)T * D * 4 : 0);
   }
+  L.stats = take((size_t)moe::stats_blocks(T) * (E + 1) * 4);
   L.total = off;
   return L;
 }
@@ -479,6 +480,25 @@ int moe_route_logits(const moe_problem* p, const float* logits, const float* sel
   ta.w = r->topk_w;
   ta.sel_bias = select_bias;
   MOE_HIP_TRY(moe::launch_topk(ta, (hipStream_t)stream), "top-K launch");
+  return MOE_OK;
+}
+
+int moe_router_stats(const moe_problem* p, const float* logits, const int32_t* expert_counts,
+                     float* stats, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  g_last_error.clear();
+  int st = check_problem(p);
+  if (st) return st;
+  if (p->T == 0) return MOE_OK;
+  MOE_CHECK_PTR(logits, "logits");
+  MOE_CHECK_PTR(expert_counts, "expert_counts");
+  MOE_CHECK_PTR(stats, "stats");
+  Layout L;
+  if ((st = check_ws(p, workspace, workspace_bytes, &L))) return st;
+  float* part = at<float>(workspace, L.stats);
+  float* zpart = part + moe::stats_blocks(p->T) * p->E;
+  MOE_HIP_TRY(moe::launch_router_stats(logits, expert_counts, p->T, p->E, p->scoring, part, zpart,
+                                       stats, (hipStream_t)stream),
+              "router statistics launch");
   return MOE_OK;
 }
 

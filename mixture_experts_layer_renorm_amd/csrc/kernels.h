@@ -136,6 +136,13 @@ hipError_t launch_gather_rows(const void* x, int64_t D, int esize, const int32_t
                               const int32_t* offsets, int E, int K, int64_t A, void* x_perm,
                               hipStream_t stream);
 
+// Router statistics: out [2E + 4] = f [E], P [E], N·Σ f P, z-loss, load CV, max/mean load.
+// part [stats_blocks(T)][E] and zpart [stats_blocks(T)] are scratch.
+int64_t stats_blocks(int64_t T);
+hipError_t launch_router_stats(const float* logits, const int32_t* counts, int64_t T, int E,
+                               int scoring, float* part, float* zpart, float* out,
+                               hipStream_t stream);
+
 // Combine / finalize.
 hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
                           const float* y_shared, const float* gate, int64_t T, int K, int D,

@@ -166,6 +166,13 @@ def test_invalid_calls_fail_before_launch(lib):
                                       None) == abi.MOE_ERR_INVALID_ARG
     assert lib.moe_update_select_bias(ctypes.byref(p), ALIGNED, ALIGNED + 4, 0.01,
                                       None) == abi.MOE_ERR_INVALID_ARG
+    # router statistics: missing inputs / output, workspace too small
+    assert lib.moe_router_stats(ctypes.byref(p), None, ALIGNED, ALIGNED, ALIGNED, need,
+                                None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_stats(ctypes.byref(p), ALIGNED, ALIGNED, None, ALIGNED, need,
+                                None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_stats(ctypes.byref(p), ALIGNED, ALIGNED, ALIGNED, ALIGNED, need - 1,
+                                None) == abi.MOE_ERR_WORKSPACE
     # dispatch / experts / combine: missing routing tensors
     assert lib.moe_dispatch(ctypes.byref(p), None, ctypes.byref(r), None, ALIGNED, need,
                             None) == abi.MOE_ERR_INVALID_ARG

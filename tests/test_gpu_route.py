@@ -205,3 +205,46 @@ def test_update_select_bias_bit_exact(E):
     torch.cuda.synchronize()
     want = O.update_select_bias(counts.numpy(), bias.numpy(), 1e-3)
     assert np.array_equal(b_dev.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+# ---- router statistics ("1.6 ..." §三 balance loss, §六 z-loss) ----
+
+def _stats_check(got, want, E):
+    np.testing.assert_allclose(f64(got["f"]), want["f"], rtol=1e-6, atol=0)
+    # P: fp32 sums of positive terms in a fixed order (at most ~ 20 + T/64 additions deep)
+    np.testing.assert_allclose(f64(got["P"]), want["P"], rtol=5e-5, atol=1e-9)
+    for k, rtol in (("aux", 5e-5), ("z", 5e-5), ("cv", 1e-6), ("max_over_mean", 1e-6)):
+        assert abs(float(got[k]) - want[k]) <= rtol * abs(want[k]) + 1e-9, (k, float(got[k]),
+                                                                           want[k])
+
+
+@pytest.mark.parametrize("T,E,K", [(1, 8, 2), (333, 8, 2), (1000, 256, 8), (4096, 256, 8),
+                                   (700, 1000, 7), (65, 64, 64)])
+@pytest.mark.parametrize("scoring", ["softmax", "sigmoid"])
+def test_router_stats_match_oracle(T, E, K, scoring):
+    g = torch.Generator().manual_seed(T + E)
+    logits = torch.randn((T, E), generator=g) * 2.0
+    idx = O.topk_select(f64(logits), K)
+    counts = torch.as_tensor(O.dispatch(idx, E)["counts"], dtype=torch.int32)
+    p = abi.make_problem(T=T, D=64, E=E, K=K, F=64, scoring=scoring)
+    got = abi.moe_router_stats(p, logits.to(DEV), counts.to(DEV), abi.alloc_workspace(p, DEV))
+    torch.cuda.synchronize()
+    _stats_check(got, O.router_stats(f64(logits), counts.numpy(), scoring), E)
+
+
+def test_router_stats_from_a_forward_pass():
+    """The statistics of a real batch: logits and counts exported by moe_forward on the skewed
+    35B-A3B-shaped layer (most assignments on 8 hot experts)."""
+    cfg = CONFIGS["skew"]
+    from mixture_experts_layer_renorm_amd.synth import make_layer
+    layer = make_layer(cfg, device=DEV, T=2048)
+    p = problem_for(cfg, T=2048)
+    r = abi.alloc_routing(p, DEV)
+    ws = abi.alloc_workspace(p, DEV)
+    out = torch.empty((2048, cfg.D), dtype=cfg.torch_dtype, device=DEV)
+    abi.moe_forward(p, layer["x"], weights_for(layer), r, out, ws)
+    got = abi.moe_router_stats(p, r["logits"], r["expert_counts"], ws)
+    torch.cuda.synchronize()
+    want = O.router_stats(f64(r["logits"]), i64(r["expert_counts"]), cfg.scoring)
+    _stats_check(got, want, cfg.E)
+    assert want["max_over_mean"] > 10  # the skew is visible in the loads
