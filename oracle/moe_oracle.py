@@ -52,7 +52,7 @@ __all__ = [
     "SCORING_SOFTMAX", "SCORING_SIGMOID",
     "as_f64", "router_logits", "shared_gate", "selection_keys", "topk_select",
     "routing_scores", "routing_weights", "topk_select_biased", "route", "update_select_bias",
-    "router_stats",
+    "router_stats", "expert_capacity",
     "dispatch", "silu", "sigmoid", "swiglu",
     "moe_forward", "moe_forward_dense_masked",
     "expert_params", "expert_flops", "expert_read_bytes", "layer_flops",
@@ -250,27 +250,49 @@ def router_stats(logits: Any, counts: Any, scoring: str = SCORING_SOFTMAX) -> Di
 # Stage 2: dispatch.  [MoE] §3.2: group the assignments by expert so each hit expert runs once.
 # ---------------------------------------------------------------------------------------------
 
-def dispatch(topk_idx: Any, E: int) -> Dict[str, np.ndarray]:
+def expert_capacity(A: int, E: int, capacity_factor: float, min_capacity: int = 0) -> int:
+    """Rows one expert may take: the even share of the batch's A = T·K assignments times the
+    capacity factor ([Satori-1.6] §三 专家容量, factor > 1 such as 1.25, leaving headroom for
+    imbalance), rounded up, and at least min_capacity (the floor of the training configuration
+    on the "Qwen3.6-27B" page, §四).  Counting assignments rather than tokens is this oracle's
+    reading for top-K routing."""
+    return max(int(min_capacity), math.ceil(capacity_factor * A / E))
+
+
+def dispatch(topk_idx: Any, E: int, capacity: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Expert-contiguous grouping of the T·K assignments a = t·K + k.
 
-    counts[e]  = number of assignments to expert e (ids outside [0,E) are sentinels, skipped)
+    counts[e]  = number of assignments kept on expert e (ids outside [0,E) are sentinels,
+                 skipped)
     offsets    = [0, cumsum(counts)]  (length E+1)
     perm[pos]  = assignment id at position pos of the grouped order; grouped by expert, ascending
                  assignment id within an expert (a stable counting sort by expert)
-    inv_perm[a]= position of assignment a, or -1 for a skipped sentinel
+    inv_perm[a]= position of assignment a, or -1 for a skipped sentinel or a dropped assignment
+    dropped    = number of assignments dropped for capacity
+
+    capacity: if given, each expert keeps only its first `capacity` assignments in that order
+    (earlier tokens first); the rest are dropped and, with no residual in the layer output,
+    contribute nothing ([Satori-1.6] §三 token dropping).
     """
     flat = np.asarray(topk_idx, dtype=np.int64).reshape(-1)
     valid = (flat >= 0) & (flat < E)
-    counts = np.bincount(flat[valid], minlength=E).astype(np.int64)
-    offsets = np.zeros(E + 1, dtype=np.int64)
-    offsets[1:] = np.cumsum(counts)
     key = np.where(valid, flat, E)          # sentinels sort after every real expert
     order = np.argsort(key, kind="stable")
-    n_valid = int(offsets[E])
-    perm = order[:n_valid]
+    raw = np.bincount(flat[valid], minlength=E).astype(np.int64)
+    kept_parts = []
+    start = 0
+    for e in range(E):
+        group = order[start:start + raw[e]]
+        start += raw[e]
+        kept_parts.append(group if capacity is None else group[:capacity])
+    perm = np.concatenate(kept_parts) if kept_parts else np.zeros(0, dtype=np.int64)
+    counts = np.array([len(g) for g in kept_parts], dtype=np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
     inv_perm = np.full(flat.shape[0], -1, dtype=np.int64)
-    inv_perm[perm] = np.arange(n_valid)
-    return {"counts": counts, "offsets": offsets, "perm": perm, "inv_perm": inv_perm}
+    inv_perm[perm] = np.arange(perm.shape[0])
+    return {"counts": counts, "offsets": offsets, "perm": perm, "inv_perm": inv_perm,
+            "dropped": int(raw.sum() - counts.sum())}
 
 
 # ---------------------------------------------------------------------------------------------
@@ -308,7 +330,8 @@ def moe_forward(x: Any, w_router: Any, w_gate_up: Sequence[Any], w_down: Sequenc
                 ws_gate_up: Optional[Any] = None, ws_down: Optional[Any] = None,
                 w_shared_gate: Optional[Any] = None,
                 logits: Optional[Any] = None,
-                select_bias: Optional[Any] = None) -> Dict[str, Any]:
+                select_bias: Optional[Any] = None,
+                capacity: Optional[int] = None) -> Dict[str, Any]:
     """Forward pass of one MoE layer, float64, without the residual.
 
     x [T,D]; w_router [E,D]; w_gate_up[e] [2F,D] and w_down[e] [D,F] are indexed one expert at a
@@ -318,6 +341,7 @@ def moe_forward(x: Any, w_router: Any, w_gate_up: Sequence[Any], w_down: Sequenc
     logits: if given (e.g. fp32 logits exported by another implementation), routing is taken
     from them instead of being recomputed from x and w_router.
     select_bias: [E] selection-only bias ([Satori-1.6] §三), or None.
+    capacity: rows per expert (see expert_capacity); dropped assignments contribute nothing.
 
     y_t = Σ_k α_{t,k} · E_{I_t[k]}(x_t) + g_t · E_s(x_t)
     """
@@ -329,7 +353,7 @@ def moe_forward(x: Any, w_router: Any, w_gate_up: Sequence[Any], w_down: Sequenc
         r = as_f64(logits)
     E = r.shape[1]
     idx, alpha = route(r, K, scoring, renormalize, select_bias)
-    d = dispatch(idx, E)
+    d = dispatch(idx, E, capacity)
     counts, offsets, perm, inv_perm = d["counts"], d["offsets"], d["perm"], d["inv_perm"]
 
     D = X.shape[1]
@@ -344,7 +368,8 @@ def moe_forward(x: Any, w_router: Any, w_gate_up: Sequence[Any], w_down: Sequenc
     y_routed = np.zeros((T, D), dtype=np.float64)
     for k in range(K):
         pos = inv_perm.reshape(T, K)[:, k]
-        y_routed += alpha[:, k:k + 1] * y_perm[pos]
+        kept = pos >= 0
+        y_routed[kept] += alpha[kept, k:k + 1] * y_perm[pos[kept]]
 
     out = y_routed.copy()
     y_shared = None

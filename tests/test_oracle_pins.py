@@ -177,6 +177,68 @@ def test_router_stats_are_distributions(scoring):
         assert abs(st["z"] - z) < 1e-12 * z
 
 
+def test_capacity_drops_the_later_assignments_by_hand():
+    """Two experts, four single-expert tokens routed 0, 0, 0, 1, capacity factor 1: each expert
+    may take ceil(1·4/2) = 2 rows, so token 2's assignment to expert 0 is dropped."""
+    C = O.expert_capacity(4, 2, 1.0)
+    assert C == 2
+    d = O.dispatch(np.array([[0], [0], [0], [1]]), 2, C)
+    assert d["counts"].tolist() == [2, 1] and d["offsets"].tolist() == [0, 2, 3]
+    assert d["perm"].tolist() == [0, 1, 3] and d["inv_perm"].tolist() == [0, 1, -1, 2]
+    assert d["dropped"] == 1
+    assert O.expert_capacity(4, 2, 1.25) == 3 and O.expert_capacity(4, 2, 1.0, 4) == 4
+    assert O.expert_capacity(512, 256, 1.25) == 3  # 2.5 rows per expert, rounded up
+
+
+def test_capacity_against_brute_force():
+    """Keep an assignment iff fewer than C earlier assignments (in a = t·K + k order) went to
+    its expert; compare with a plain loop over the assignments."""
+    rng = np.random.default_rng(42)
+    T, E, K = 200, 10, 3
+    idx = O.topk_select(rng.standard_normal((T, E)) + np.linspace(0, 2, E), K)
+    idx[rng.random(idx.shape) < 0.05] = -1
+    for C in (1, 5, 30, 60, 10 ** 6):
+        d = O.dispatch(idx, E, C)
+        seen = [0] * E
+        kept = []
+        for a, e in enumerate(idx.reshape(-1)):
+            if 0 <= e < E:
+                if seen[e] < C:
+                    kept.append((e, a))
+                seen[e] += 1
+        kept.sort()  # by expert, then by assignment id
+        assert d["perm"].tolist() == [a for _, a in kept]
+        assert d["counts"].tolist() == [min(n, C) for n in seen]
+        assert d["dropped"] == sum(seen) - sum(min(n, C) for n in seen)
+        inv = np.full(T * K, -1)
+        inv[[a for _, a in kept]] = np.arange(len(kept))
+        assert d["inv_perm"].tolist() == inv.tolist()
+    # a capacity above every load changes nothing
+    assert all(np.array_equal(O.dispatch(idx, E, 10 ** 6)[k], O.dispatch(idx, E)[k])
+               for k in ("counts", "offsets", "perm", "inv_perm"))
+
+
+def test_capacity_in_the_layer_output():
+    """A dropped assignment contributes nothing; the token keeps its other slots' terms with
+    their original weights (no renormalisation after dropping)."""
+    rng = np.random.default_rng(43)
+    x, wr, wgu, wd, _ = _tiny_layer(rng, T=9, D=8, E=3, F=4)
+    K = 2
+    full = O.moe_forward(x, wr, wgu, wd, K)
+    cap = O.moe_forward(x, wr, wgu, wd, K, capacity=2)
+    idx, alpha = full["topk_idx"], full["topk_w"]
+    want = np.zeros_like(full["out"])
+    seen = [0] * 3
+    for t in range(9):
+        for k in range(K):
+            e = idx[t, k]
+            if seen[e] < 2:
+                want[t] += alpha[t, k] * _swiglu_torch(x[t:t + 1], wgu[e], wd[e])[0]
+            seen[e] += 1
+    np.testing.assert_allclose(cap["out"], want, rtol=1e-12, atol=1e-12)
+    assert cap["counts"].sum() == 6 and not np.allclose(cap["out"], full["out"])
+
+
 def test_worked_example_output():
     """y = u + g2·FFN2(u) + g5·FFN5(u); the layer output is everything but the residual u."""
     g = _golden("worked_example_e5_k2.json")
