@@ -82,6 +82,13 @@ typedef struct {
   int32_t out_dtype;    /* moe_dtype of `out`; accumulation is always fp32, and a bf16
                            output is the round-to-nearest-even of the fp32 result         */
   uint32_t flags;       /* MOE_FLAG_*                                                      */
+  float capacity_factor;/* 0: dropless.  > 0: each expert keeps at most
+                           C = max(min_capacity, ceil(capacity_factor * T*K / E)) rows
+                           ("1.6 ..." §三 expert capacity; the ceiling is taken in double on
+                           the host): its first C assignments in ascending a = t*K + k; the
+                           others are dropped (inv_perm = -1, excluded from counts) and add
+                           nothing to the output                                           */
+  int32_t min_capacity; /* floor of C when capacity_factor > 0 (>= 0)                      */
 } moe_problem;
 
 /* Weights, all in `dtype` except logit_bias (fp32).  Layouts follow the fused projections of
@@ -108,11 +115,12 @@ typedef struct {
                               expert id; ids outside [0,E) are skipped
                               by dispatch and combine (sentinels)                          */
   float *topk_w;           /* [T, K] fp32 weights a_t,e                                    */
-  int32_t *expert_counts;  /* [E]   t_e = assignments routed to expert e                   */
+  int32_t *expert_counts;  /* [E]   t_e = assignments routed to (and kept on) expert e     */
   int32_t *expert_offsets; /* [E+1] exclusive prefix sum of expert_counts                  */
   int32_t *perm;           /* [T*K] perm[pos] = assignment id a = t*K + k, grouped by
                               expert, ascending a within an expert (first offsets[E] valid) */
-  int32_t *inv_perm;       /* [T*K] inv_perm[a] = pos, or -1 for a skipped sentinel        */
+  int32_t *inv_perm;       /* [T*K] inv_perm[a] = pos, or -1 for a skipped sentinel or an
+                              assignment dropped for capacity                              */
   float *shared_gate;      /* [T]   g_t = sigmoid(w_s . x_t)                               */
 } moe_routing;
 

@@ -47,7 +47,8 @@ class moe_problem(ctypes.Structure):
                 ("K", ctypes.c_int32), ("F", ctypes.c_int32), ("F_shared", ctypes.c_int32),
                 ("shared_gated", ctypes.c_int32), ("scoring", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("capacity_factor", ctypes.c_float),
+                ("min_capacity", ctypes.c_int32)]
 
 
 _WEIGHT_FIELDS = ("w_router", "logit_bias", "w_gate_up", "w_down", "ws_gate_up", "ws_down",
@@ -121,7 +122,8 @@ def _check(status: int) -> None:
 def make_problem(T: int, D: int, E: int, K: int, F: int, F_shared: int = 0,
                  shared_gated: bool = False, scoring: str = "softmax", dtype=torch.bfloat16,
                  out_dtype=None, atomic_combine: bool = False,
-                 renormalize: bool = True) -> moe_problem:
+                 renormalize: bool = True, capacity_factor: float = 0.0,
+                 min_capacity: int = 0) -> moe_problem:
     if scoring not in ("softmax", "sigmoid"):
         raise ValueError(f"scoring must be 'softmax' or 'sigmoid', got {scoring!r}")
     out_dtype = dtype if out_dtype is None else out_dtype
@@ -130,7 +132,8 @@ def make_problem(T: int, D: int, E: int, K: int, F: int, F_shared: int = 0,
     return moe_problem(T=T, D=D, E=E, K=K, F=F, F_shared=F_shared,
                        shared_gated=1 if shared_gated else 0,
                        scoring=MOE_SCORE_SOFTMAX if scoring == "softmax" else MOE_SCORE_SIGMOID,
-                       dtype=_DTYPE_CODE[dtype], out_dtype=_DTYPE_CODE[out_dtype], flags=flags)
+                       dtype=_DTYPE_CODE[dtype], out_dtype=_DTYPE_CODE[out_dtype], flags=flags,
+                       capacity_factor=capacity_factor, min_capacity=min_capacity)
 
 
 def problem_dtype(p: moe_problem) -> torch.dtype:

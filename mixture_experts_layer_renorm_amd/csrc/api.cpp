@@ -2,7 +2,9 @@
 // the order of kernel launches for each stage.  No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
+#include <climits>
 #include <cstdlib>
 #include <cstdio>
 #include <cstring>
@@ -56,6 +58,9 @@ int check_problem(const moe_problem* p) {
     return fail(MOE_ERR_INVALID_ARG, "shared_gated must be 0 or 1");
   if (p->flags & ~(uint32_t)(MOE_FLAG_ATOMIC_COMBINE | MOE_FLAG_NO_RENORM))
     return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
+  if (!(p->capacity_factor >= 0.0f) || p->capacity_factor > 1e6f)
+    return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be in [0, 1e6]");
+  if (p->min_capacity < 0) return fail(MOE_ERR_INVALID_ARG, "min_capacity < 0");
   if (p->D % 64 || p->F % 64 || p->F_shared % 64)
     return fail(MOE_ERR_UNSUPPORTED, "D, F and F_shared must be multiples of 64 (D=%d F=%d Fs=%d)",
                 p->D, p->F, p->F_shared);
@@ -67,6 +72,15 @@ int check_problem(const moe_problem* p) {
 }
 
 bool has_shared(const moe_problem* p) { return p->F_shared > 0; }
+
+// Rows each expert may keep (INT32_MAX when dropless).
+int32_t capacity(const moe_problem* p) {
+  if (!(p->capacity_factor > 0.0f)) return INT32_MAX;
+  const double c = std::ceil((double)p->capacity_factor * (double)(p->T * p->K) / p->E);
+  const double lim = (double)INT32_MAX;
+  const double v = c > lim ? lim : c;
+  return v > p->min_capacity ? (int32_t)v : p->min_capacity;
+}
 bool gated(const moe_problem* p) { return p->F_shared > 0 && p->shared_gated; }
 
 // Grouped (routed-expert) GEMMs.  The host does not see the per-expert counts (no sync), so the
@@ -535,7 +549,8 @@ int moe_dispatch(const moe_problem* p, const void* x, moe_routing* r, void* x_pe
   const int64_t A = p->T * p->K;
   MOE_HIP_TRY(moe::launch_dispatch(r->topk_idx, A, p->E, at<int32_t>(workspace, L.seg_counts),
                                    r->expert_counts, r->expert_offsets, r->perm, r->inv_perm,
-                                   moe::TileSplit{32, 32, -1, 0}, nullptr, nullptr, s),
+                                   capacity(p), moe::TileSplit{32, 32, -1, 0}, nullptr, nullptr,
+                                   s),
               "dispatch launch");
   if (x_perm)
     MOE_HIP_TRY(moe::launch_gather_rows(x, p->D, (int)esize(p->dtype), r->perm, r->expert_offsets,
@@ -671,7 +686,8 @@ int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_
   MOE_HIP_TRY(mark(MOE_STAGE_DISPATCH), "event record");
   MOE_HIP_TRY(moe::launch_dispatch(r.topk_idx, A, p->E, at<int32_t>(ws, L.seg_counts),
                                    r.expert_counts, r.expert_offsets, r.perm, r.inv_perm,
-                                   tile_split(plan, L.max_mtiles), tiles, tile_count, s),
+                                   capacity(p), tile_split(plan, L.max_mtiles), tiles,
+                                   tile_count, s),
               "dispatch launch");
   // 3. routed gate_up with SiLU*up
   void* H = at<void>(ws, L.H);

@@ -12,9 +12,13 @@
 //             and the grouped-GEMM tile map.
 //   scatter : each wave re-reads its segment 64 ids at a time.  Lanes holding the same expert
 //             find each other with one ballot per bit of the expert id; a lane's rank among its
-//             lower-numbered peers plus the running position of its expert (in LDS) is its
-//             output position.  Segments, rounds and lanes all follow ascending a, so the sort
-//             is stable and the result bit-exact.
+//             lower-numbered peers plus the running rank of its expert (in LDS) is its rank
+//             q within the expert, and offsets[e] + q its output position.  Segments, rounds
+//             and lanes all follow ascending a, so the sort is stable and the result
+//             bit-exact.
+// Expert capacity ("1.6 混合专家（MoE）" §三): with a cap C, scan counts min(t_e, C) rows per
+// expert (so offsets and tile maps cover only kept rows) and scatter drops every assignment
+// whose rank q is C or more (inv_perm = -1): each expert keeps its first C assignments.
 #include <cstdlib>
 #include <cstring>
 
@@ -128,7 +132,7 @@ __device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, const
 }
 
 __global__ void __launch_bounds__(kScanThreads) scan_kernel(int32_t* __restrict__ seg_counts,
-                                                            int64_t nseg, int E,
+                                                            int64_t nseg, int E, int cap,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets,
                                                             const TileSplit ts,
@@ -168,11 +172,11 @@ __global__ void __launch_bounds__(kScanThreads) scan_kernel(int32_t* __restrict_
       for (int u = 0; u < 16; ++u) v[u] = s + u < s1 ? seg_counts[(s + u) * E + e] : 0;
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        if (s + u < s1) seg_counts[(s + u) * E + e] = run;  // the segment's base in expert e
+        if (s + u < s1) seg_counts[(s + u) * E + e] = run;  // the segment's first rank in e
         run += v[u];
       }
     }
-    if (c == P - 1) cnt[e] = run;
+    if (c == P - 1) cnt[e] = run < cap ? run : cap;  // rows kept
   }
   __syncthreads();
   // expert offsets
@@ -211,7 +215,7 @@ __global__ void __launch_bounds__(kScanThreads) tile_map_kernel(const int32_t* _
 }
 
 __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ idx, int64_t A,
-                                                      int E, int nbits, int64_t nseg,
+                                                      int E, int nbits, int cap, int64_t nseg,
                                                       const int32_t* __restrict__ seg_base,
                                                       const int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ perm,
@@ -220,7 +224,8 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t seg = (int64_t)blockIdx.x * 4 + wave;
   if (seg >= nseg) return;
-  int* run = run_all + wave * E;
+  int* run = run_all + wave * 2 * E;  // next rank within each expert
+  int* off = run + E;                  // expert offsets
   const int64_t a0 = seg * kSegLen;
   int ev[kSegRounds];
 #pragma unroll
@@ -228,7 +233,10 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
     const int64_t a = a0 + r * 64 + lane;
     ev[r] = a < A ? idx[a] : -1;
   }
-  for (int e = lane; e < E; e += 64) run[e] = offsets[e] + seg_base[seg * E + e];
+  for (int e = lane; e < E; e += 64) {
+    run[e] = seg_base[seg * E + e];
+    off[e] = offsets[e];
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -246,9 +254,14 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
     if (valid) {
       const int rank = __popcll(peers & lt);
       const int base = run[e];
-      const int pos = base + rank;
-      perm[pos] = (int32_t)a;
-      inv_perm[a] = pos;
+      const int q = base + rank;  // rank of this assignment within its expert
+      if (q < cap) {
+        const int pos = off[e] + q;
+        perm[pos] = (int32_t)a;
+        inv_perm[a] = pos;
+      } else {
+        inv_perm[a] = -1;  // over capacity: dropped
+      }
       if (rank == 0) run[e] = base + __popcll(peers);
     } else if (a < A) {
       inv_perm[a] = -1;
@@ -267,11 +280,12 @@ constexpr int kFusedWaves = kScanThreads / 64;
 constexpr int kFusedBatch = 8;  // 64-id rounds whose loads are issued together
 
 __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
-    const int32_t* __restrict__ idx, int64_t A, int E, int nbits, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ idx, int64_t A, int E, int nbits, int cap,
+    int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
     const TileSplit ts, int32_t* __restrict__ tiles, int32_t* __restrict__ tile_count) {
   extern __shared__ int sm[];
-  int* hist = sm;                       // [kFusedWaves][E]: counts, then running positions
+  int* hist = sm;                       // [kFusedWaves][E]: counts, then running ranks
   int* cnt = hist + kFusedWaves * E;    // [E]
   int* off = cnt + E;                   // [E]
   int* scratch = off + E;               // [32]
@@ -302,7 +316,7 @@ __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
       hist[w * E + e] = run;
       run += c;
     }
-    cnt[e] = run;
+    cnt[e] = run < cap ? run : cap;  // rows kept
   }
   __syncthreads();
   int total = 0;
@@ -321,7 +335,6 @@ __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
   if (threadIdx.x == 0) offsets[E] = total;
   __syncthreads();
   if (tiles) build_tiles(cnt, off, E, ts, scratch, tiles, tile_count);
-  for (int i = threadIdx.x; i < kFusedWaves * E; i += kScanThreads) hist[i] += off[i % E];
   __syncthreads();
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t b0 = a_begin; b0 < a_end; b0 += 64 * kFusedBatch) {
@@ -345,9 +358,14 @@ __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
       if (valid) {
         const int rank = __popcll(peers & lt);
         const int base = h[e];
-        const int pos = base + rank;
-        perm[pos] = (int32_t)a;
-        inv_perm[a] = pos;
+        const int q = base + rank;  // rank within the expert
+        if (q < cap) {
+          const int pos = off[e] + q;
+          perm[pos] = (int32_t)a;
+          inv_perm[a] = pos;
+        } else {
+          inv_perm[a] = -1;  // over capacity: dropped
+        }
         if (rank == 0) h[e] = base + __popcll(peers);
       } else if (a < a_end) {
         inv_perm[a] = -1;
@@ -390,7 +408,7 @@ int64_t dispatch_num_segments(int64_t A) { return (A + kSegLen - 1) / kSegLen; }
 
 hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_counts,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                           const TileSplit& ts, int32_t* tiles, int32_t* tile_count,
+                           int cap, const TileSplit& ts, int32_t* tiles, int32_t* tile_count,
                            hipStream_t stream) {
   const int64_t nseg = dispatch_num_segments(A);
   int nbits = 1;
@@ -398,7 +416,7 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_co
   if (dispatch_fused(A, E)) {
     const size_t lds = (size_t)((kFusedWaves + 2) * E + 32) * sizeof(int);
     hipLaunchKernelGGL(dispatch_fused_kernel, dim3(1), dim3(kScanThreads), lds, stream, idx, A,
-                       E, nbits, counts, offsets, perm, inv_perm, ts, tiles, tile_count);
+                       E, nbits, cap, counts, offsets, perm, inv_perm, ts, tiles, tile_count);
     return hipGetLastError();
   }
   const dim3 g((unsigned)((nseg + 3) / 4)), b(256);
@@ -408,11 +426,11 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_co
   if (err != hipSuccess) return err;
   const size_t lds_scan = (size_t)(2 * E + kScanThreads + 32) * sizeof(int);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), lds_scan, stream, seg_counts, nseg,
-                     E, counts, offsets, ts, tiles, tile_count);
+                     E, cap, counts, offsets, ts, tiles, tile_count);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(scatter_kernel, g, b, lds_waves, stream, idx, A, E, nbits, nseg, seg_counts,
-                     offsets, perm, inv_perm);
+  hipLaunchKernelGGL(scatter_kernel, g, b, 2 * lds_waves, stream, idx, A, E, nbits, cap, nseg,
+                     seg_counts, offsets, perm, inv_perm);
   return hipGetLastError();
 }
 

@@ -125,9 +125,11 @@ int64_t dispatch_num_segments(int64_t A);
 // True when launch_dispatch runs as one work-group (small batches; MOE_DISPATCH=fused|multi
 // overrides).
 bool dispatch_fused(int64_t A, int E);
+// cap: rows each expert keeps (its first cap assignments in ascending id; the others get
+// inv_perm = -1 and are not counted); INT32_MAX for none.
 hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_counts,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                           const TileSplit& ts, int32_t* tiles, int32_t* tile_count,
+                           int cap, const TileSplit& ts, int32_t* tiles, int32_t* tile_count,
                            hipStream_t stream);
 // Tile maps from offsets alone (staged API).
 hipError_t launch_tile_map(const int32_t* offsets, int E, const TileSplit& ts, int32_t* tiles,

@@ -92,6 +92,12 @@ def test_workspace_size_and_validation(lib):
     p = _prob()
     p.flags = 0x80
     assert _ws_size(lib, p)[0] == abi.MOE_ERR_INVALID_ARG
+    # capacity: negative or NaN factor, negative floor
+    assert _ws_size(lib, _prob(capacity_factor=-1.0))[0] == abi.MOE_ERR_INVALID_ARG
+    assert _ws_size(lib, _prob(capacity_factor=float("nan")))[0] == abi.MOE_ERR_INVALID_ARG
+    assert _ws_size(lib, _prob(capacity_factor=1.25, min_capacity=-3))[0] == \
+        abi.MOE_ERR_INVALID_ARG
+    assert _ws_size(lib, _prob(capacity_factor=1.25, min_capacity=4))[0] == abi.MOE_OK
     assert lib.moe_workspace_size(None, None) == abi.MOE_ERR_INVALID_ARG
     assert b"NULL" in lib.moe_last_error()
     # the workspace grows with T; the atomic combine needs no [T*K, D] row buffer

@@ -12,9 +12,10 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run_dispatch(idx: torch.Tensor, E: int, x=None, D=64):
+def _run_dispatch(idx: torch.Tensor, E: int, x=None, D=64, capacity_factor=0.0, min_capacity=0):
     T, K = idx.shape
-    p = abi.make_problem(T=T, D=D, E=E, K=K, F=64)
+    p = abi.make_problem(T=T, D=D, E=E, K=K, F=64, capacity_factor=capacity_factor,
+                         min_capacity=min_capacity)
     r = abi.alloc_routing(p, DEV, logits=False)
     r["topk_idx"] = idx.to(DEV, torch.int32).contiguous()
     x_perm = None
@@ -101,3 +102,25 @@ def test_dispatch_both_paths(monkeypatch, path, T, E, K):
     if T > 1:
         idx[torch.rand(idx.shape, generator=g) < 0.05] = -1  # sentinels
     _check(idx, E)
+
+
+# Expert capacity: each expert keeps its first C assignments; the rest are dropped.
+@pytest.mark.parametrize("path", ["fused", "multi"])
+@pytest.mark.parametrize("T,E,K,cf,minc", [(64, 8, 2, 1.0, 0), (1023, 7, 3, 0.5, 0),
+                                           (4096, 256, 8, 1.25, 4), (3000, 128, 4, 1.0, 40),
+                                           (20000, 64, 8, 1.1, 0), (50, 16, 4, 0.01, 0)])
+def test_dispatch_capacity(monkeypatch, path, T, E, K, cf, minc):
+    monkeypatch.setenv("MOE_DISPATCH", path)
+    g = torch.Generator().manual_seed(200 + T + E)
+    hot = [i * max(1, E // 8) for i in range(min(8, E))]
+    idx = _topk_like(T, E, K, g, hot, 0.3)  # skewed, so hot experts overflow
+    idx[torch.rand(idx.shape, generator=g) < 0.03] = -1
+    r, _ = _run_dispatch(idx, E, capacity_factor=cf, min_capacity=minc)
+    C = O.expert_capacity(T * K, E, float(np.float32(cf)), minc)
+    want = O.dispatch(i64(idx), E, C)
+    assert want["dropped"] > 0
+    n = int(want["offsets"][E])
+    np.testing.assert_array_equal(i64(r["expert_counts"]), want["counts"])
+    np.testing.assert_array_equal(i64(r["expert_offsets"]), want["offsets"])
+    np.testing.assert_array_equal(i64(r["perm"])[:n], want["perm"])
+    np.testing.assert_array_equal(i64(r["inv_perm"]), want["inv_perm"])

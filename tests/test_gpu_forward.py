@@ -200,3 +200,34 @@ def test_forward_with_select_bias(name):
     plain = O.topk_select(f64(r["logits"]), cfg.K)
     assert np.any(np.sort(ref["topk_idx"], 1) != np.sort(plain, 1))  # the bias mattered
     assert rel_max_err(out, ref["out"]) <= _tol(cfg)
+
+
+@pytest.mark.parametrize("name,cf", [("tiny", 0.75), ("a3b_E16", 1.0), ("skew_E64", 1.25),
+                                     ("a3b_decode", 2.0), ("a17b_E32", 0.5)])
+@pytest.mark.parametrize("atomic", [False, True])
+def test_forward_with_capacity(name, cf, atomic):
+    """Token dropping: routing and the kept rows bit-exact against the oracle with the same
+    capacity, dropped slots contributing nothing (a token with every slot dropped and no shared
+    expert outputs exactly 0), output within the layer's tolerance.  The tolerance is taken on
+    the scale of the layer's dropless output: dropping removes terms (on the skewed layer most
+    of the large hot-expert ones), which shrinks the output RMS but not the rounding of the
+    terms that remain."""
+    cfg, layer, T = _case(name)
+    p = problem_for(cfg, T=T, out_dtype=torch.float32, atomic_combine=atomic)
+    p.capacity_factor = cf
+    r = abi.alloc_routing(p, DEV)
+    out = torch.empty((T, cfg.D), dtype=torch.float32, device=DEV)
+    abi.moe_forward(p, layer["x"], weights_for(layer), r, out, abi.alloc_workspace(p, DEV))
+    torch.cuda.synchronize()
+    C = O.expert_capacity(T * cfg.K, cfg.E, cf)
+    args, kw = oracle_args(cfg, layer)
+    ref = O.moe_forward(*args, logits=f64(r["logits"]), capacity=C, **kw)
+    _check_routing(cfg, r, ref)
+    assert int(ref["counts"].max()) <= C
+    full = O.moe_forward(*args, logits=f64(r["logits"]), **kw)["out"]
+    scale = float(np.sqrt(np.mean(full ** 2)))
+    err = float(np.max(np.abs(f64(out) - ref["out"]))) / scale
+    assert err <= _tol(cfg), f"{name}: max|err|/RMS(dropless) = {err:.3e}"
+    all_dropped = np.all(ref["inv_perm"].reshape(T, cfg.K) < 0, axis=1)
+    if not cfg.F_shared and all_dropped.any():
+        assert np.all(f64(out)[all_dropped] == 0.0)
