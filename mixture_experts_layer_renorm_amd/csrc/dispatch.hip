@@ -96,6 +96,10 @@ __global__ void __launch_bounds__(256) count_kernel(const int32_t* __restrict__ 
 // Builds the tile maps from per-expert counts held in LDS.  One entry per M tile:
 // {expert, first row position, rows, 0, first M tile of the expert, M tiles of the expert};
 // experts with more than ts.split rows go to map 1 (bm1-row tiles), the others to map 0.
+// An expert's rows are split evenly over its ceil(c / bm) M tiles (the first c % mt tiles one
+// row more): its tiles then cost the same, run in step on one XCD and fetch each weight tile
+// once into its L2 for all of them (a full tile and a short last one drift apart, and each
+// streams the weights from memory by itself).
 __device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, const TileSplit ts,
                             int* scratch, int32_t* tiles, int32_t* tile_count) {
   int32_t* maps[2] = {tiles, tiles + ts.map1_entries * kTileStride};
@@ -111,11 +115,12 @@ __device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, const
       const int mt = which == m ? (c + bm - 1) / bm : 0;
       int chunk_total;
       const int first = block_exclusive_scan(mt, scratch, &chunk_total) + total[m];
+      const int base_rows = mt > 0 ? c / mt : 0, extra = mt > 0 ? c % mt : 0;
       for (int q = 0; q < mt; ++q) {
         int32_t* ent = maps[m] + (int64_t)(first + q) * kTileStride;
         ent[0] = e;
-        ent[1] = off_lds[e] + q * bm;
-        ent[2] = min(bm, c - q * bm);
+        ent[1] = off_lds[e] + q * base_rows + min(q, extra);
+        ent[2] = base_rows + (q < extra ? 1 : 0);
         ent[3] = 0;
         ent[4] = first;
         ent[5] = mt;

@@ -2,10 +2,11 @@
 // receive hundreds of rows or more, and the shared expert, which sees every token.  There a
 // tile's weights are reused by many rows ("S23-J10" §3: a group's intensity is about t_e FLOP
 // per weight byte), so the limit is the MFMA pipes, and the kernel is shaped to keep them fed:
-//  * 4 waves (one per SIMD) over a 256 x 256 output tile; each wave owns 128 x 128 as 8 x 8
-//    MFMA tiles of 16 x 16 (v_mfma_f32_16x16x32_bf16) with its 256 accumulators in the AGPRs.
-//    Per 32-wide K slice a wave reads 8 A and 8 B fragments (16 KiB of LDS) for 64 MFMAs, so
-//    LDS bandwidth stays at half of what the matrix pipes consume.
+//  * 8 waves (two per SIMD) over a 256 x 256 output tile, 4 along M x 2 along N; each wave
+//    owns 64 x 128 as 4 x 8 MFMA tiles of 16 x 16 (v_mfma_f32_16x16x32_bf16).  Per 32-wide K
+//    step a wave reads 4 A and 8 B fragments (12 KiB of LDS) for 32 MFMAs.  A tile with fewer
+//    rows runs with fewer 16-row MFMA tiles per wave (64-row granularity), so a group's
+//    partly filled last tile costs in proportion to its rows.
 //  * K advances 64 per stage (128 bytes of every row, so each row's line is requested once).
 //    Both operands move from L2/HBM straight into LDS with global_load_lds_dwordx4 (no staging
 //    registers), token rows in a 2-stage ring and weights, which stream from HBM, in a
@@ -56,14 +57,14 @@ __device__ __forceinline__ void barrier_after() {
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// One stage of one operand (256 rows x 128 bytes) by one of NW waves: instruction i fills
-// staged rows [8 (wave + NW i), +8); src holds the lane's 32-bit byte offsets from base.
-template <int NW>
+// One stage of one operand (up to 256 rows x 128 bytes) by one of NW waves: instruction i fills
+// staged rows [8 (wave + NW i), +8), so the first N instructions of the 8 waves fill rows
+// [0, 64 N); src holds the lane's 32-bit byte offsets from base.
+template <int NW, int N = kBM / 8 / NW>
 __device__ __forceinline__ void dma_operand(const char* base, const uint32_t* src, uint32_t off,
                                             char* stage, int wave) {
-  constexpr int kDma = kBM / 8 / NW;
 #pragma unroll
-  for (int i = 0; i < kDma; ++i)
+  for (int i = 0; i < N; ++i)
     __builtin_amdgcn_global_load_lds(base + (src[i] + off), stage + (wave + NW * i) * 1024, 16,
                                      0, 0);
 }
@@ -85,59 +86,232 @@ __device__ __forceinline__ void read_frags(const char* la, const char* lb, bf16x
   for (int j = 0; j < 8; ++j) bfr[j] = *(const bf16x8*)(lb + boff<SWIGLU>(j));
 }
 
-// 64 MFMAs of one stage, reading the next stage's fragments in between: B fragments into the
-// other B set during rows 0..3, A fragment i in place right after row i's 8 MFMAs.
+// The 8·MI MFMAs of one 32-wide K step, reading the next step's fragments in between: one of
+// the 8 next B fragments (into the other B set) after every MI MFMAs, A fragment i in place
+// right after row i's 8 MFMAs.
 template <int MI, bool SWIGLU>
 __device__ __forceinline__ void mma_stage(f32x4 (*acc)[8], bf16x8* af, const bf16x8* bfr,
                                           const char* la_n, const char* lb_n, bf16x8* bfr_n) {
-  static_assert(MI >= 4, "the next B fragments are read during rows 0..3");
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      if (i < 4 && (j & 3) == 3) bfr_n[2 * i + (j >> 2)] = *(const bf16x8*)(lb_n + boff<SWIGLU>(2 * i + (j >> 2)));
+      if ((i * 8 + j + 1) % MI == 0) {
+        const int b = (i * 8 + j + 1) / MI - 1;
+        bfr_n[b] = *(const bf16x8*)(lb_n + boff<SWIGLU>(b));
+      }
     }
     af[i] = *(const bf16x8*)(la_n + i * 16 * kRow);
   }
 }
 
-// WM waves along M (2: four waves of 128 x 128, one per SIMD, accumulators in AGPRs; 4: eight
-// waves of 64 x 128, two per SIMD).
-template <int WM, int S, int EPI>
-__global__ void __launch_bounds__(128 * WM)
-__attribute__((amdgpu_waves_per_eu(WM / 2, WM / 2))) mfma_kernel(const GemmParams p) {
-  constexpr int NW = 2 * WM, kNT = 64 * NW;
-  constexpr int MI = kBM / 16 / WM;         // 16-row MFMA tiles per wave
-  constexpr int kDma = kBM / 8 / NW;  // 1 KiB DMA instructions per wave per operand stage
+constexpr int kNW = 8;                 // waves: 4 along M x 2 along N
+constexpr int kNT = 64 * kNW;          // threads
+constexpr int kDma = kBM / 8 / kNW;    // 1 KiB DMA instructions per wave per full operand stage
+
+// One output tile.  Wave (wm, wn) owns rows [16 MIA wm, +16 MIA) and columns [128 wn, +128) as
+// MIA x 8 MFMA tiles of 16 x 16; a tile of `rows` rows runs with MIA = ceil(rows / 64), so a
+// partly filled tile (a group's last one) costs MIA/4 of a full one: the two waves that share
+// a SIMD own different row blocks, and only the token rows [0, 64 MIA) are fetched.
+template <int MIA, int EPI>
+__device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int tid, int wave,
+                                          int group, int row_start, int rows, int n_tile,
+                                          int ns) {
   constexpr bool kSwiglu = EPI == EPI_SWIGLU;
-  static_assert(S == kSB && 4 * kDma < 64, "vmcnt range");
-
-  __shared__ __attribute__((aligned(1024))) char smem[kLds];
-  char* const sA = smem;                    // token-row ring, kSA stages
-  char* const sB = smem + kSA * kAStage;    // weight ring, kSB stages
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;  // WM x 2 waves; wave tile (16 MI) x 128
+  static_assert(MIA >= 1 && MIA <= 4 && kDma == 4 && 4 * kDma < 64, "tile shape, vmcnt range");
+  char* const sA = smem;                  // token-row ring, kSA stages
+  char* const sB = smem + kSA * kAStage;  // weight ring, kSB stages
+  const int lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 15, lk = lane >> 4;
 
-  constexpr int BNE = kSwiglu ? kBN / 2 : kBN;  // output columns per tile
+  // Lane offsets (within a stage) of this wave's first A and B fragment rows, for each 32-wide
+  // half of the stage.  For SwiGLU the tile's first 128 B rows are gate rows and the next 128
+  // the matching up rows, and a wave's column tiles j and j + 4 are a gate/up pair.
+  const int la_row = (wm * MIA * 16 + lr) * kRow;
+  const int lb_row = ((kSwiglu ? wn * 64 : wn * 128) + lr) * kRow;
+  const int ch0 = (lk ^ swz(lr)) << 4, ch1 = ((4 + lk) ^ swz(lr)) << 4;
+
+  // ---- global source of each DMA chunk this lane issues per stage ----------------------------
+  const char* gbase = p.B + (int64_t)group * p.b_group_bytes;
+  uint32_t srcA[kDma], srcB[kDma];
+#pragma unroll
+  for (int i = 0; i < kDma; ++i) {
+    const int r = 8 * (wave + kNW * i) + (lane >> 3);  // staged row of either operand
+    const int chunk = (lane & 7) ^ swz(r);            // logical chunk kept in this slot
+    const int pos = row_start + min(r, rows - 1);
+    const int arow = p.a_gather ? p.a_gather[pos] / p.a_div : pos;
+    srcA[i] = (uint32_t)arow * (uint32_t)p.lda_bytes + chunk * 16;
+    int brow;
+    if (kSwiglu) {
+      const int n = n_tile * (kBN / 2) + (r & (kBN / 2 - 1));
+      brow = n < p.N ? (r < kBN / 2 ? n : p.N + n) : 0;
+    } else {
+      const int n = n_tile * kBN + r;
+      brow = n < p.N ? n : 0;
+    }
+    srcB[i] = (uint32_t)brow * (uint32_t)p.ldb_bytes + chunk * 16;
+  }
+
+  f32x4 acc[MIA][8];
+#pragma unroll
+  for (int i = 0; i < MIA; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // every wave is done with the previous tile's LDS (epilogue staging) before new DMA lands
+  barrier_after<0, 0>();
+  // Ring schedule (per wave, in issue order): prologue A0 B0 A1 B1 B2, then before stage g+1
+  // is used, A(g+2) B(g+3).  Token rows run two stages ahead, weights three, so up to 64 KiB
+  // of weights per CU are in flight.  A stage of token rows is MIA instructions per wave, one
+  // of weights kDma; the waits below count exactly those.
+  dma_operand<kNW, MIA>(p.A, srcA, 0, sA, wave);
+  dma_operand<kNW>(gbase, srcB, 0, sB, wave);
+  if (ns > 1) {
+    dma_operand<kNW, MIA>(p.A, srcA, kRow, sA + kAStage, wave);
+    dma_operand<kNW>(gbase, srcB, kRow, sB + kBStage, wave);
+  }
+  if (ns > 2) dma_operand<kNW>(gbase, srcB, 2 * kRow, sB + 2 * kBStage, wave);
+
+  // stage 0 published, its first half's fragments read (A fragments are refilled in place,
+  // B fragments alternate between two sets)
+  bf16x8 af0[MIA], bf0[8], bf1[8];
+  if (ns > 2)  // A1 B1 B2 were issued after B0 and may still fly
+    barrier_after<MIA + 2 * kDma, 0>();
+  else
+    barrier_after<0, 0>();
+  read_frags<MIA, kSwiglu>(sA + la_row + ch0, sB + lb_row + ch0, af0, bf0);
+
+  // Stage g's MFMAs: first half (step 2g) while reading the second half's fragments from
+  // the same stage; then publish stage g+1 (this wave's copies landed; every wave has read
+  // all of stage g, so its buffers are free), refill them with A(g+2) and B(g+3), and run the
+  // second half (step 2g+1) while reading stage g+1's first half.
+  for (int g = 0; g < ns; ++g) {
+    const char* ca = sA + (g % kSA) * kAStage;
+    const char* cb = sB + (g % kSB) * kBStage;
+    mma_stage<MIA, kSwiglu>(acc, af0, bf0, ca + la_row + ch1, cb + lb_row + ch1, bf1);
+    if (g + 1 < ns) {
+      if (g + 2 < ns)  // B(g+2) went out after A(g+1) and may still fly
+        barrier_after<kDma, 0>();
+      else
+        barrier_after<0, 0>();
+      if (g + 2 < ns)
+        dma_operand<kNW, MIA>(p.A, srcA, (uint32_t)(g + 2) * kRow, sA + (g % kSA) * kAStage,
+                              wave);
+      if (g + 3 < ns)
+        dma_operand<kNW>(gbase, srcB, (uint32_t)(g + 3) * kRow, sB + (g % kSB) * kBStage, wave);
+    }
+    // after the last stage these reads fetch unused leftovers
+    const char* na = sA + ((g + 1) % kSA) * kAStage;
+    const char* nb = sB + ((g + 1) % kSB) * kBStage;
+    mma_stage<MIA, kSwiglu>(acc, af0, bf1, na + la_row + ch0, nb + lb_row + ch0, bf0);
+  }
+
+  // ---- epilogue (staged in the ring's LDS) ---------------------------------------------------
+  // Lane (lr, lk) holds rows 16 (MIA wm + i) + 4 lk + r of column tile j in acc[i][j][r].  The
+  // thread index is laundered through an empty asm so the store offsets below are computed
+  // here, not hoisted out of the tile loop into registers (and spilled).
+  constexpr int kWaveRows = MIA * 16;  // rows per wave row block
+  int etid = tid;
+  asm volatile("" : "+v"(etid));
+  const int elr = etid & 15, elk = (etid >> 4) & 3;
+  barrier_after<0, 0>();  // all waves are done reading the ring
+  if constexpr (kSwiglu) {
+    // H tile: up to 256 rows x 128 columns of the layer dtype, 272-byte LDS rows
+    constexpr int kLdH = kBN / 2 + 8;
+    __bf16* Eh = (__bf16*)smem;
+#pragma unroll
+    for (int i = 0; i < MIA; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = wm * kWaveRows + i * 16 + elk * 4 + r;
+          const int col = wn * 64 + j * 16 + elr;
+          Eh[row * kLdH + col] = (__bf16)(silu_fast(acc[i][j][r]) * acc[i][j + 4][r]);
+        }
+    barrier_after<0, 0>();
+    constexpr int kCpr = kBN / 2 / 8;  // 16 chunks of 8 values per H row
+    char* Ht = (char*)p.C + ((int64_t)row_start * p.ldc + n_tile * (kBN / 2)) * 2;
+    const int ncols = min(kBN / 2, p.N - n_tile * (kBN / 2));
+#pragma unroll
+    for (int mm = 0; mm < 4 * kWaveRows * kCpr / kNT; ++mm) {
+      const int c = etid + kNT * mm;
+      const int row = c / kCpr, ch = c % kCpr;
+      if (row < rows && ch * 8 < ncols)
+        *(bf16x8*)(Ht + (uint32_t)(row * (int)p.ldc + ch * 8) * 2u) =
+            *(const bf16x8*)(Eh + row * kLdH + ch * 8);
+    }
+  } else if constexpr (EPI == EPI_STORE) {
+    // fp32 tile in four passes, one per wave row block (up to 64 rows x 256 columns, 1040-byte
+    // LDS rows), each written to LDS by the two waves that own it
+    constexpr int kLdE = kBN + 4;
+    float* E = (float*)smem;
+    char* Ct = (char*)p.C + ((int64_t)row_start * p.ldc + n_tile * kBN) * 4;
+    const float* rs = p.row_scale ? p.row_scale + row_start : nullptr;
+    const int ncols = min(kBN, p.N - n_tile * kBN);
+    constexpr int kCpr = kBN / 4;  // 16-byte chunks per fp32 row
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      if (pass * kWaveRows < rows) {  // uniform
+        if (wm == pass) {
+#pragma unroll
+          for (int i = 0; i < MIA; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                E[(i * 16 + elk * 4 + r) * kLdE + wn * 128 + j * 16 + elr] = acc[i][j][r];
+        }
+        barrier_after<0, 0>();
+#pragma unroll
+        for (int mm = 0; mm < kWaveRows * kCpr / kNT; ++mm) {
+          const int c = etid + kNT * mm;
+          const int lrow = c / kCpr, col = (c % kCpr) * 4;
+          const int row = pass * kWaveRows + lrow;
+          if (row < rows && col < ncols) {
+            f32x4 v = *(const f32x4*)(E + lrow * kLdE + col);
+            if (rs) v *= rs[row];
+            *(f32x4*)(Ct + (uint32_t)(row * (int)p.ldc + col) * 4u) = v;
+          }
+        }
+        barrier_after<0, 0>();
+      }
+    }
+  } else {  // EPI_ATOMIC_COMBINE
+#pragma unroll
+    for (int i = 0; i < MIA; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * kWaveRows + i * 16 + elk * 4 + r;
+        if (row >= rows) continue;
+        const int a = p.perm[row_start + row];
+        const float w = p.topk_w[a];
+        float* dst = p.acc_out + (int64_t)(a / p.topk) * p.ldo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int n = n_tile * kBN + wn * 128 + j * 16 + elr;
+          if (n < p.N) unsafeAtomicAdd(dst + n, w * acc[i][j][r]);
+        }
+      }
+  }
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mfma_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLds];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  constexpr int BNE = EPI == EPI_SWIGLU ? kBN / 2 : kBN;  // output columns per tile
   const int ntN = (p.N + BNE - 1) / BNE;
   const int mt_total = p.tiles ? load_uniform(p.tile_count, 0) : (p.M + kBM - 1) / kBM;
   const int nt = mt_total * ntN;
   const int xcd = blockIdx.x % kXcds, per = gridDim.x / kXcds, jb = blockIdx.x / kXcds;
   const int lo = (int)((int64_t)nt * xcd / kXcds), hi = (int)((int64_t)nt * (xcd + 1) / kXcds);
-  const int nk = p.Kdim / 32;  // MFMA K steps (even: Kdim is a multiple of 64)
-  const int ns = nk / 2;       // DMA stages
-
-  // Lane offsets (within a stage) of this wave's first A and B fragment rows, for each 32-wide
-  // half of the stage.  B rows follow the 256 A rows; for SwiGLU the tile's first 128 B rows
-  // are gate rows and the next 128 the matching up rows, and a wave's column tiles j and j + 4
-  // are a gate/up pair.
-  const int la_row = (wm * MI * 16 + lr) * kRow;
-  const int lb_row = ((kSwiglu ? wn * 64 : wn * 128) + lr) * kRow;
-  const int ch0 = (lk ^ swz(lr)) << 4, ch1 = ((4 + lk) ^ swz(lr)) << 4;
+  const int ns = p.Kdim / 64;  // DMA stages (Kdim is a multiple of 64)
 
   for (int t = lo + jb; t < hi; t += per) {
     // ---- logical tile: expert-major, then N tile, then M tile -------------------------------
@@ -156,175 +330,22 @@ __attribute__((amdgpu_waves_per_eu(WM / 2, WM / 2))) mfma_kernel(const GemmParam
       row_start = load_uniform(p.tiles, m * kTileStride + 1);
       rows = load_uniform(p.tiles, m * kTileStride + 2);
     }
-
-    // ---- global source of each DMA chunk this lane issues per stage --------------------------
-    const char* gbase = p.B + (int64_t)group * p.b_group_bytes;
-    uint32_t srcA[kDma], srcB[kDma];
-#pragma unroll
-    for (int i = 0; i < kDma; ++i) {
-      const int r = 8 * (wave + NW * i) + (lane >> 3);  // staged row of either operand
-      const int chunk = (lane & 7) ^ swz(r);           // logical chunk kept in this slot
-      const int pos = row_start + min(r, rows - 1);
-      const int arow = p.a_gather ? p.a_gather[pos] / p.a_div : pos;
-      srcA[i] = (uint32_t)arow * (uint32_t)p.lda_bytes + chunk * 16;
-      int brow;
-      if (kSwiglu) {
-        const int n = n_tile * (kBN / 2) + (r & (kBN / 2 - 1));
-        brow = n < p.N ? (r < kBN / 2 ? n : p.N + n) : 0;
-      } else {
-        const int n = n_tile * kBN + r;
-        brow = n < p.N ? n : 0;
-      }
-      srcB[i] = (uint32_t)brow * (uint32_t)p.ldb_bytes + chunk * 16;
-    }
-
-    f32x4 acc[MI][8];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // every wave is done with the previous tile's LDS (epilogue staging) before new DMA lands
-    barrier_after<0, 0>();
-    // Ring schedule (per wave, in issue order): prologue A0 B0 A1 B1 B2, then before stage g+1
-    // is used, A(g+2) B(g+3).  Token rows run two stages ahead, weights three, so up to 64 KiB
-    // of weights per CU are in flight.
-    dma_operand<NW>(p.A, srcA, 0, sA, wave);
-    dma_operand<NW>(gbase, srcB, 0, sB, wave);
-    if (ns > 1) {
-      dma_operand<NW>(p.A, srcA, kRow, sA + kAStage, wave);
-      dma_operand<NW>(gbase, srcB, kRow, sB + kBStage, wave);
-    }
-    if (ns > 2) dma_operand<NW>(gbase, srcB, 2 * kRow, sB + 2 * kBStage, wave);
-
-    // stage 0 published, its first half's fragments read (A fragments are refilled in place,
-    // B fragments alternate between two sets)
-    bf16x8 af0[MI], bf0[8], bf1[8];
-    if (ns > 2)  // A1 B1 B2 were issued after B0 and may still fly
-      barrier_after<3 * kDma, 0>();
-    else
-      barrier_after<0, 0>();
-    read_frags<MI, kSwiglu>(sA + la_row + ch0, sB + lb_row + ch0, af0, bf0);
-
-    // Stage g's MFMAs: first half (step 2g) while reading the second half's fragments from
-    // the same stage; then publish stage g+1 (this wave's copies landed; every wave has read
-    // all of stage g, so its buffers are free), refill them with A(g+2) and B(g+3), and run the
-    // second half (step 2g+1) while reading stage g+1's first half.
-    for (int g = 0; g < ns; ++g) {
-      const char* ca = sA + (g % kSA) * kAStage;
-      const char* cb = sB + (g % kSB) * kBStage;
-      mma_stage<MI, kSwiglu>(acc, af0, bf0, ca + la_row + ch1, cb + lb_row + ch1, bf1);
-      if (g + 1 < ns) {
-        if (g + 2 < ns)  // B(g+2) went out after A(g+1) and may still fly
-          barrier_after<kDma, 0>();
-        else
-          barrier_after<0, 0>();
-        if (g + 2 < ns)
-          dma_operand<NW>(p.A, srcA, (uint32_t)(g + 2) * kRow, sA + (g % kSA) * kAStage, wave);
-        if (g + 3 < ns)
-          dma_operand<NW>(gbase, srcB, (uint32_t)(g + 3) * kRow, sB + (g % kSB) * kBStage,
-                          wave);
-      }
-      // after the last stage these reads fetch unused leftovers
-      const char* na = sA + ((g + 1) % kSA) * kAStage;
-      const char* nb = sB + ((g + 1) % kSB) * kBStage;
-      mma_stage<MI, kSwiglu>(acc, af0, bf1, na + la_row + ch0, nb + lb_row + ch0, bf0);
-    }
-
-    // ---- epilogue (staged in the ring's LDS) -------------------------------------------------
-    // Lane (lr, lk) holds rows i*16 + lk*4 + r of column tile j in acc[i][j][r].
-    barrier_after<0, 0>();  // all waves are done reading the ring
-    if constexpr (kSwiglu) {
-      // H tile: 256 rows x 128 columns of the layer dtype, 272-byte LDS rows
-      constexpr int kLdH = kBN / 2 + 8;
-      __bf16* Eh = (__bf16*)smem;
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = wm * MI * 16 + i * 16 + lk * 4 + r;
-            const int col = wn * 64 + j * 16 + lr;
-            Eh[row * kLdH + col] = (__bf16)(silu_fast(acc[i][j][r]) * acc[i][j + 4][r]);
-          }
-      barrier_after<0, 0>();
-      constexpr int kCpr = kBN / 2 / 8;  // 16 chunks of 8 values per H row
-      char* Ht = (char*)p.C + ((int64_t)row_start * p.ldc + n_tile * (kBN / 2)) * 2;
-      const int ncols = min(kBN / 2, p.N - n_tile * (kBN / 2));
-#pragma unroll
-      for (int mm = 0; mm < kBM * kCpr / kNT; ++mm) {
-        const int c = tid + kNT * mm;
-        const int row = c / kCpr, ch = c % kCpr;
-        if (row < rows && ch * 8 < ncols)
-          *(bf16x8*)(Ht + (uint32_t)(row * (int)p.ldc + ch * 8) * 2u) =
-              *(const bf16x8*)(Eh + row * kLdH + ch * 8);
-      }
-    } else if constexpr (EPI == EPI_STORE) {
-      // fp32 tile in passes of 64 rows x 256 columns (1040-byte LDS rows); pass q holds row
-      // blocks 4 q .. 4 q + 3, written by the two waves that own them
-      constexpr int kLdE = kBN + 4;
-      float* E = (float*)smem;
-      char* Ct = (char*)p.C + ((int64_t)row_start * p.ldc + n_tile * kBN) * 4;
-      const float* rs = p.row_scale ? p.row_scale + row_start : nullptr;
-      const int ncols = min(kBN, p.N - n_tile * kBN);
-      constexpr int kCpr = kBN / 4;  // 16-byte chunks per fp32 row
-#pragma unroll
-      for (int pass = 0; pass < 4; ++pass) {
-        if (pass * 64 < rows) {  // uniform
-          if (wm == pass * 4 / MI) {
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-              for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  E[(ii * 16 + lk * 4 + r) * kLdE + wn * 128 + j * 16 + lr] =
-                      acc[(pass * 4) % MI + ii][j][r];
-          }
-          barrier_after<0, 0>();
-#pragma unroll
-          for (int mm = 0; mm < 64 * kCpr / kNT; ++mm) {
-            const int c = tid + kNT * mm;
-            const int lrow = c / kCpr, col = (c % kCpr) * 4;
-            const int row = pass * 64 + lrow;
-            if (row < rows && col < ncols) {
-              f32x4 v = *(const f32x4*)(E + lrow * kLdE + col);
-              if (rs) v *= rs[row];
-              *(f32x4*)(Ct + (uint32_t)(row * (int)p.ldc + col) * 4u) = v;
-            }
-          }
-          barrier_after<0, 0>();
-        }
-      }
-    } else {  // EPI_ATOMIC_COMBINE
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = wm * MI * 16 + i * 16 + lk * 4 + r;
-          if (row >= rows) continue;
-          const int a = p.perm[row_start + row];
-          const float w = p.topk_w[a];
-          float* dst = p.acc_out + (int64_t)(a / p.topk) * p.ldo;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int n = n_tile * kBN + wn * 128 + j * 16 + lr;
-            if (n < p.N) unsafeAtomicAdd(dst + n, w * acc[i][j][r]);
-          }
-        }
+    switch ((rows + 63) >> 6) {  // 16-row MFMA tiles per wave that hold rows
+      case 1:
+        mfma_tile<1, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns);
+        break;
+      case 2:
+        mfma_tile<2, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns);
+        break;
+      case 3:
+        mfma_tile<3, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns);
+        break;
+      default:
+        mfma_tile<4, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns);
+        break;
     }
   }
 }
-
-#ifndef MOE_MFMA_WM
-#define MOE_MFMA_WM 4
-#endif
-constexpr int kWM = MOE_MFMA_WM;  // waves along M
-#ifndef MOE_MFMA_S
-#define MOE_MFMA_S 3
-#endif
-constexpr int kS = MOE_MFMA_S;    // ring stages
 
 template <int EPI>
 hipError_t launch_epi(const GemmParams& p, int64_t max_mtiles, hipStream_t stream) {
@@ -334,8 +355,7 @@ hipError_t launch_epi(const GemmParams& p, int64_t max_mtiles, hipStream_t strea
   int64_t grid = want < kCus ? want : kCus;
   grid = ((grid + kXcds - 1) / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
-  hipLaunchKernelGGL((mfma_kernel<kWM, kS, EPI>), dim3((unsigned)grid), dim3(128 * kWM), 0, stream,
-                     p);
+  hipLaunchKernelGGL((mfma_kernel<EPI>), dim3((unsigned)grid), dim3(kNT), 0, stream, p);
   return hipGetLastError();
 }
 
