@@ -194,7 +194,10 @@ Layout layout(const moe_problem* p) {
     L.y_perm = L.y_shared = 0;
   } else {
     L.acc = 0;
-    L.y_perm = take((size_t)A * D * 4);
+    // fp32 rows, or fp16 rows (256-byte aligned) followed by their fp32 block factors
+    const size_t f32_rows = (size_t)A * D * 4;
+    const size_t f16_rows = ((size_t)A * D * 2 + 255) / 256 * 256 + (size_t)A * ((D + 255) / 256) * 4;
+    L.y_perm = take(f32_rows > f16_rows ? f32_rows : f16_rows);
     L.y_shared = take(has_shared(p) ? (size_t)T * D * 4 : 0);
   }
   L.stats = take((size_t)moe::stats_blocks(T) * (E + 1) * 4);
@@ -309,8 +312,8 @@ hipError_t run_gate_up(const moe_problem* p, const void* x, const void* x_perm, 
 
 hipError_t run_down(const moe_problem* p, const void* H, const void* w_d, const int32_t* tiles,
                     const int32_t* tile_count, int64_t max_mtiles, const GroupedPlan& plan,
-                    float* y_perm, float* acc, const int32_t* perm, const float* topk_w,
-                    hipStream_t s) {
+                    void* y_perm, float* acc, const int32_t* perm, const float* topk_w,
+                    hipStream_t s, float* y_scale = nullptr) {
   const size_t es = esize(p->dtype);
   moe::GemmParams g{};
   g.A = (const char*)H;
@@ -323,6 +326,8 @@ hipError_t run_down(const moe_problem* p, const void* H, const void* w_d, const 
   if (y_perm) {
     g.C = y_perm;
     g.ldc = p->D;
+    g.c_scale = y_scale;  // fp16 rows with block factors (see compact_rows)
+    g.ldcs = (p->D + 255) / 256;
     return launch_grouped(p, plan, moe::EPI_STORE, g, tiles, tile_count, max_mtiles, s);
   }
   g.acc_out = acc;
@@ -331,6 +336,20 @@ hipError_t run_down(const moe_problem* p, const void* H, const void* w_d, const 
   g.topk_w = topk_w;
   g.topk = p->K;
   return launch_grouped(p, plan, moe::EPI_ATOMIC_COMBINE, g, tiles, tile_count, max_mtiles, s);
+}
+
+// Whether moe_forward keeps the routed expert rows (y_perm) as fp16 with a power-of-two factor
+// per row and 256-column block instead of fp32: for bf16 layers whose grouped GEMMs are the
+// streaming / matrix-core kernels (the only ones with that epilogue).  Half the bytes of the
+// down GEMM's stores and of the combine's reads; the factor keeps every value below 2^15, so
+// nothing overflows, and the 11-bit significand adds about 2^-12 of a block's largest value,
+// far below the bf16 rounding of H.
+bool compact_rows(const moe_problem* p, const GroupedPlan& plan) {
+  auto ok = [](moe::TileCfg c) {
+    return c == moe::TILE_STREAM_64 || c == moe::TILE_STREAM_128 || c == moe::TILE_STREAM_192 ||
+           c == moe::TILE_MFMA;
+  };
+  return p->dtype == MOE_DTYPE_BF16 && ok(plan.cfg0) && (plan.split < 0 || ok(plan.cfg1));
 }
 
 // Shared expert on all T tokens: Hs = SwiGLU gate/up of x; out = row_scale * (Hs Ws_downᵀ).
@@ -426,8 +445,11 @@ const char* moe_describe_plan(const moe_problem* p) {
             name(grouped_plan(p).cfg1) + " (larger)";
   if (has_shared(p))
     text += "; shared: " + name(dense_cfg(p->T, (int64_t)2 * p->F_shared, p->dtype));
-  text += (p->flags & MOE_FLAG_ATOMIC_COMBINE) ? "; combine: fp32 atomics in the down epilogue"
-                                               : "; combine: gather in slot order";
+  text += (p->flags & MOE_FLAG_ATOMIC_COMBINE)
+              ? "; combine: fp32 atomics in the down epilogue"
+              : compact_rows(p, grouped_plan(p))
+                    ? "; combine: gather in slot order over fp16 rows with block factors"
+                    : "; combine: gather in slot order";
   return text.c_str();
 }
 
@@ -705,13 +727,27 @@ int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_
       MOE_HIP_TRY(run_shared(p, x, w, at<void>(ws, L.Hs), y_shared, nullptr, s),
                   "shared expert launch");
     MOE_HIP_TRY(mark(MOE_STAGE_DOWN), "event record");
-    MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, plan, y_perm, nullptr,
-                         nullptr, nullptr, s),
-                "down GEMM launch");
-    MOE_HIP_TRY(mark(MOE_STAGE_FINAL), "event record");
-    MOE_HIP_TRY(moe::launch_combine(y_perm, r.inv_perm, r.topk_w, y_shared, gate, p->T, p->K,
-                                    p->D, out, p->out_dtype, s),
-                "combine launch");
+    if (compact_rows(p, plan)) {
+      // fp16 rows [A, D], then the fp32 block factors [A, ceil(D / 256)] (256-byte aligned)
+      const int nblk = (p->D + 255) / 256;
+      float* y_scale = reinterpret_cast<float*>(
+          reinterpret_cast<char*>(y_perm) + ((A * p->D * 2 + 255) / 256) * 256);
+      MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, plan, y_perm,
+                           nullptr, nullptr, nullptr, s, y_scale),
+                  "down GEMM launch");
+      MOE_HIP_TRY(mark(MOE_STAGE_FINAL), "event record");
+      MOE_HIP_TRY(moe::launch_combine16(y_perm, y_scale, nblk, r.inv_perm, r.topk_w, y_shared,
+                                        gate, p->T, p->K, p->D, out, p->out_dtype, s),
+                  "combine launch");
+    } else {
+      MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, plan, y_perm,
+                           nullptr, nullptr, nullptr, s),
+                  "down GEMM launch");
+      MOE_HIP_TRY(mark(MOE_STAGE_FINAL), "event record");
+      MOE_HIP_TRY(moe::launch_combine(y_perm, r.inv_perm, r.topk_w, y_shared, gate, p->T, p->K,
+                                      p->D, out, p->out_dtype, s),
+                  "combine launch");
+    }
     MOE_HIP_TRY(mark(MOE_STAGE_COUNT), "event record");
     return MOE_OK;
   }

@@ -4,7 +4,8 @@
 // combine : deterministic gather-sum.  One work-group per token: the K rows of the token's
 //           expert outputs are read through inv_perm and summed in slot order in fp32, the
 //           shared branch is added with its gate, and the sum is rounded once to the output
-//           dtype.  16-byte loads along D.
+//           dtype.  16-byte loads along D.  combine16 reads the same rows stored as fp16 with
+//           a power-of-two factor per 256-column block.
 // cast    : fp32 accumulator -> output dtype (round to nearest even), for the atomic path.
 // zero    : fill an fp32 accumulator with +0.0 (a kernel, not a memset node).
 #include "kernels.h"
@@ -56,6 +57,60 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   }
 }
 
+__device__ __forceinline__ void store8(float* dst, const float* a) {
+  *(float4*)dst = make_float4(a[0], a[1], a[2], a[3]);
+  *(float4*)(dst + 4) = make_float4(a[4], a[5], a[6], a[7]);
+}
+__device__ __forceinline__ void store8(__bf16* dst, const float* a) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (__bf16)a[i];
+  *(bf16x8*)dst = o;
+}
+
+// Gather-sum over fp16 expert rows with per-(row, 256-column block) factors: 8 columns per
+// thread (one 16-byte load per slot), in slot order, then the shared branch, one rounding.
+template <typename OUT>
+__global__ void __launch_bounds__(256) combine16_kernel(const _Float16* __restrict__ y16,
+                                                        const float* __restrict__ ysc, int nblk,
+                                                        const int32_t* __restrict__ inv_perm,
+                                                        const float* __restrict__ topk_w,
+                                                        const float* __restrict__ y_shared,
+                                                        const float* __restrict__ gate, int64_t T,
+                                                        int K, int D, OUT* __restrict__ out) {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    const float g = y_shared ? (gate ? gate[t] : 1.0f) : 0.0f;
+    for (int d = threadIdx.x * 8; d < D; d += blockDim.x * 8) {
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        const int pos = inv_perm[t * K + k];
+        if (pos < 0) continue;  // sentinel or dropped assignment
+        const float w = topk_w[t * K + k] * ysc[(int64_t)pos * nblk + (d >> 8)];
+        const f16x8 v = *(const f16x8*)(y16 + (int64_t)pos * D + d);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += w * (float)v[i];
+      }
+      if (y_shared) {
+        const float4 a = *(const float4*)(y_shared + t * D + d);
+        const float4 b = *(const float4*)(y_shared + t * D + d + 4);
+        acc[0] += g * a.x;
+        acc[1] += g * a.y;
+        acc[2] += g * a.z;
+        acc[3] += g * a.w;
+        acc[4] += g * b.x;
+        acc[5] += g * b.y;
+        acc[6] += g * b.z;
+        acc[7] += g * b.w;
+      }
+      store8(out + t * D + d, acc);
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256) cast_bf16_kernel(const float* __restrict__ src,
                                                         __bf16* __restrict__ dst, int64_t n4) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
@@ -89,6 +144,22 @@ hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const fl
   else
     hipLaunchKernelGGL(combine_kernel<float>, g, b, 0, stream, y_perm, inv_perm, topk_w, y_shared,
                        gate, T, K, D, (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine16(const void* y16, const float* ysc, int nblk, const int32_t* inv_perm,
+                            const float* topk_w, const float* y_shared, const float* gate,
+                            int64_t T, int K, int D, void* out, int out_dtype,
+                            hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  const int64_t cap = (int64_t)kCus * 16;
+  const dim3 g((unsigned)(T < cap ? T : cap)), b(256);
+  if (out_dtype == 1)
+    hipLaunchKernelGGL(combine16_kernel<__bf16>, g, b, 0, stream, (const _Float16*)y16, ysc, nblk,
+                       inv_perm, topk_w, y_shared, gate, T, K, D, (__bf16*)out);
+  else
+    hipLaunchKernelGGL(combine16_kernel<float>, g, b, 0, stream, (const _Float16*)y16, ysc, nblk,
+                       inv_perm, topk_w, y_shared, gate, T, K, D, (float*)out);
   return hipGetLastError();
 }
 

@@ -20,9 +20,10 @@
 //  * Token rows are gathered through the dispatch permutation by the DMA addresses themselves.
 //  * Persistent, XCD-aware schedule over logical tiles ordered expert-major, then N tile, then
 //    M tile, so the tiles that share an expert's weights or rows meet in one XCD's L2.
-//  * Epilogues are assembled in LDS (reusing the ring) and leave as 16-byte chunks: fused
+//  * Epilogues are assembled in LDS (reusing the ring) and leave as whole chunks: fused
 //    SiLU·up (a wave's 8 column tiles are 4 gate/up pairs), fp32 store with an optional row
-//    scale, or the weighted fp32 atomic combine.
+//    scale, fp16 store with one power-of-two factor per tile, or the weighted fp32 atomic
+//    combine.
 #include "kernels.h"
 #include "silu.h"
 
@@ -31,6 +32,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256;       // tile rows (tokens)
 constexpr int kBN = 256;       // tile weight rows (output columns; half of them for SwiGLU)
@@ -248,7 +250,28 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
     // LDS rows), each written to LDS by the two waves that own it
     constexpr int kLdE = kBN + 4;
     float* E = (float*)smem;
+    // fp16 rows: one power-of-two factor for the tile, from its largest |value| (reduced over
+    // the lane, the wave, then the 8 waves through LDS past the staging area)
+    float sc = 1.0f, inv = 1.0f;
+    if (p.c_scale) {
+      float* tmax = (float*)(smem + kLds - 64);
+      float mx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < MIA; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[i][j][r]));
+      mx = wave_max_abs(mx);
+      if ((etid & 63) == 0) tmax[wave] = mx;
+      barrier_after<0, 0>();
+      mx = tmax[0];
+#pragma unroll
+      for (int w = 1; w < kNW; ++w) mx = fmaxf(mx, tmax[w]);
+      f16_block_scale(mx, &sc, &inv);
+    }
     char* Ct = (char*)p.C + ((int64_t)row_start * p.ldc + n_tile * kBN) * 4;
+    char* Ch = (char*)p.C + ((int64_t)row_start * p.ldc + n_tile * kBN) * 2;
     const float* rs = p.row_scale ? p.row_scale + row_start : nullptr;
     const int ncols = min(kBN, p.N - n_tile * kBN);
     constexpr int kCpr = kBN / 4;  // 16-byte chunks per fp32 row
@@ -268,9 +291,20 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
 #pragma unroll
         for (int mm = 0; mm < kWaveRows * kCpr / kNT; ++mm) {
           const int c = etid + kNT * mm;
-          const int lrow = c / kCpr, col = (c % kCpr) * 4;
+          const int lrow = c / kCpr, col = (c % kCpr) * 4;  // one row per wave
           const int row = pass * kWaveRows + lrow;
-          if (row < rows && col < ncols) {
+          if (p.c_scale) {
+            // fp16 with the tile's power-of-two factor
+            const f32x4 v = *(const f32x4*)(E + lrow * kLdE + col);
+            if (row < rows) {
+              if (col < ncols) {
+                const f16x4 h = {(_Float16)(v[0] * sc), (_Float16)(v[1] * sc),
+                                 (_Float16)(v[2] * sc), (_Float16)(v[3] * sc)};
+                *(f16x4*)(Ch + (uint32_t)(row * (int)p.ldc + col) * 2u) = h;
+              }
+              if ((etid & 63) == 0) p.c_scale[(int64_t)(row_start + row) * p.ldcs + n_tile] = inv;
+            }
+          } else if (row < rows && col < ncols) {
             f32x4 v = *(const f32x4*)(E + lrow * kLdE + col);
             if (rs) v *= rs[row];
             *(f32x4*)(Ct + (uint32_t)(row * (int)p.ldc + col) * 4u) = v;

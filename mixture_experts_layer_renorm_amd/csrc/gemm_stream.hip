@@ -21,9 +21,10 @@
 //  * When the step count is a multiple of P the ring runs on across tiles: the last round of a
 //    tile fetches the first P steps of the next, whose loads then overlap this tile's
 //    epilogue.
-//  * Epilogues: fused SiLU·up (gate_up; a wave's 32 columns are 16 gate/up pairs), fp32 row
-//    store (down), both staged in LDS and written as whole 16-byte chunks, or the weighted
-//    fp32 atomic combine (down, opt-in).
+//  * Epilogues: fused SiLU·up (gate_up; a wave's 32 columns are 16 gate/up pairs), row store
+//    (down: fp32, or fp16 with one power-of-two factor per tile, so that max|v| < 2^15), both
+//    staged in LDS and written as whole chunks, or the weighted fp32 atomic combine (down,
+//    opt-in).
 #include "kernels.h"
 #include "silu.h"
 
@@ -32,6 +33,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRow = 128;  // bytes per token row per K step (64 bf16)
 // s_waitcnt immediate (gfx9 layout) that waits for vmcnt == 0 and leaves expcnt/lgkmcnt free.
@@ -98,6 +100,7 @@ __global__ void __launch_bounds__(512) stream_kernel(const GemmParams p) {
                            : EPI == EPI_SWIGLU ? BM * kLdH * 2
                                                : 16;
   __shared__ __attribute__((aligned(16))) char ep[kEpBytes];
+  __shared__ float tmax[8];  // per-wave maxima of the fp16 row store
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -308,8 +311,28 @@ __global__ void __launch_bounds__(512) stream_kernel(const GemmParams p) {
       __syncthreads();
     } else if constexpr (EPI == EPI_STORE) {
       float* E = (float*)ep;
+      // fp16 rows: one power-of-two factor for the tile, from its largest |value| (reduced
+      // over the lane, the wave, then the 8 waves through LDS)
+      float sc = 1.0f, inv = 1.0f;
+      if (p.c_scale) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[i][j][r]));
+        mx = wave_max_abs(mx);
+        if ((etid & 63) == 0) tmax[wave] = mx;
+        __syncthreads();
+        mx = tmax[0];
+#pragma unroll
+        for (int w = 1; w < 8; ++w) mx = fmaxf(mx, tmax[w]);
+        f16_block_scale(mx, &sc, &inv);
+      }
       // tile origin (uniform) + 32-bit lane offsets
       char* Ct = (char*)p.C + ((int64_t)cur.row_start * p.ldc + cur.n_tile * BN) * 4;
+      char* Ch = (char*)p.C + ((int64_t)cur.row_start * p.ldc + cur.n_tile * BN) * 2;
       const float* rs = p.row_scale ? p.row_scale + cur.row_start : nullptr;
       const int ncols = min(BN, p.N - cur.n_tile * BN);
       constexpr int kCpr = BN / 4;  // 16-byte chunks per fp32 row
@@ -329,9 +352,20 @@ __global__ void __launch_bounds__(512) stream_kernel(const GemmParams p) {
 #pragma unroll
           for (int m = 0; m < kEpRows * kCpr / NT; ++m) {
             const int c = etid + NT * m;
-            const int lrow = c / kCpr, col = (c % kCpr) * 4;
+            const int lrow = c / kCpr, col = (c % kCpr) * 4;  // one row per wave
             const int row = q * kEpRows + lrow;
-            if (row < cur.rows && col < ncols) {
+            if (p.c_scale) {
+              // fp16 with the tile's power-of-two factor
+              const f32x4 v = *(const f32x4*)(E + lrow * kLdE + col);
+              if (row < cur.rows) {
+                if (col < ncols) {
+                  const f16x4 h = {(_Float16)(v[0] * sc), (_Float16)(v[1] * sc),
+                                   (_Float16)(v[2] * sc), (_Float16)(v[3] * sc)};
+                  *(f16x4*)(Ch + (uint32_t)(row * (int)p.ldc + col) * 2u) = h;
+                }
+                if ((etid & 63) == 0) p.c_scale[(int64_t)(cur.row_start + row) * p.ldcs + cur.n_tile] = inv;
+              }
+            } else if (row < cur.rows && col < ncols) {
               f32x4 v = *(const f32x4*)(E + lrow * kLdE + col);
               if (rs) v *= rs[row];
               *(f32x4*)(Ct + (uint32_t)(row * (int)p.ldc + col) * 4u) = v;

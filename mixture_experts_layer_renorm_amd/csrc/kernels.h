@@ -45,8 +45,13 @@ struct GemmParams {
   const int32_t* tile_count;
   int32_t M;
   // Epilogue operands.
-  void* C;                  // STORE: fp32 [rows, ldc]; SWIGLU: dtype [rows, ldc]
+  void* C;                  // STORE: fp32 [rows, ldc] (or fp16 with c_scale); SWIGLU: dtype
   int64_t ldc;
+  float* c_scale;           // STORE, streaming and matrix-core GEMMs only: if set, C holds fp16
+                            // values scaled by a power of two per output tile (tile max
+                            // < 2^15), and c_scale[row * ldcs + n_tile] the factor that
+                            // restores row `row` of N tile n_tile (256 columns)
+  int64_t ldcs;
   float* C2;                // STORE: column N (if B2) -> C2[row]
   const float* col_bias;    // STORE: + col_bias[n]
   const float* row_scale;   // STORE: * row_scale[row]
@@ -145,10 +150,33 @@ hipError_t launch_router_stats(const float* logits, const int32_t* counts, int64
                                int scoring, float* part, float* zpart, float* out,
                                hipStream_t stream);
 
+__device__ __forceinline__ float wave_max_abs(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// Power-of-two scale of one block of values for fp16 storage: s with max|v| * s < 2^15 (so
+// no value overflows fp16) and its exact inverse.  max_abs = 0 gives s = 2^15.
+__device__ __forceinline__ void f16_block_scale(float max_abs, float* s, float* inv) {
+  int ex = 0;
+  (void)frexpf(max_abs, &ex);  // max_abs = f * 2^ex with f in [0.5, 1)
+  int e = 15 - ex;
+  e = e < -126 ? -126 : (e > 126 ? 126 : e);
+  *s = ldexpf(1.0f, e);
+  *inv = ldexpf(1.0f, -e);
+}
+
 // Combine / finalize.
 hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
                           const float* y_shared, const float* gate, int64_t T, int K, int D,
                           void* out, int out_dtype, hipStream_t stream);
+// The same combine over fp16 expert rows y16 [T*K, D] with block factors ysc [T*K, nblk]
+// (nblk = ceil(D / 256)); each term is (topk_w * factor) * value, summed in slot order.
+hipError_t launch_combine16(const void* y16, const float* ysc, int nblk, const int32_t* inv_perm,
+                            const float* topk_w, const float* y_shared, const float* gate,
+                            int64_t T, int K, int D, void* out, int out_dtype,
+                            hipStream_t stream);
 hipError_t launch_cast(const float* src, void* dst, int64_t n, int out_dtype, hipStream_t stream);
 hipError_t launch_zero(float* dst, int64_t n, hipStream_t stream);
 

@@ -44,6 +44,9 @@ CASES = {
     "max_E_K": ("a3b_prefill", {"D": 128, "E": 1024, "K": 64, "F": 64}, 40),
     # reduction lengths that are not a multiple of the streaming ring, ragged N tiles
     "odd_k": ("a3b_prefill", {"D": 192, "F": 320, "E": 16}, 300),
+    # expert outputs far above the fp16 range (|y| ~ 1e5): the fp16 rows of the default path
+    # carry a power-of-two factor per 256-column block, so nothing overflows
+    "huge_values": ("tiny", {"dtype": "bf16", "std_expert": 4.0, "D": 320}, 200),
 }
 
 
