@@ -85,9 +85,10 @@ bool gated(const moe_problem* p) { return p->F_shared > 0 && p->shared_gated; }
 
 // Grouped (routed-expert) GEMMs.  The host does not see the per-expert counts (no sync), so the
 // dispatch kernel sorts the experts into two tile maps on the device: experts with up to 192
-// rows are bound by reading their weights and go to the weight-streaming GEMM (64-row M tiles
-// when the mean group is decode-sized, 192 otherwise); larger groups reuse each weight byte
-// hundreds of times and go to the matrix-core GEMM (256 x 256 tiles).  No expert can have
+// rows are bound by reading their weights and go to the weight-streaming GEMM (192-row M
+// tiles); larger groups reuse each weight byte hundreds of times and go to the matrix-core GEMM
+// (256 x 256 tiles).  Decode-sized batches (mean group <= 24 rows) run every group on the
+// matrix-core GEMM.  No expert can have
 // more than T rows, so for T <= 192 the second map is not built.  fp32 layers (and operands
 // of 4 GiB or more) use the tile GEMM with one map.  MOE_GROUPED_TILE (small, large, stream64,
 // stream128, stream192, mfma) forces one map with the named tile, for tuning and for tests
@@ -122,9 +123,12 @@ GroupedPlan grouped_plan(const moe_problem* p) {
   const int64_t A = p->T * p->K;
   const double mean = (double)A / p->E;
   if (bf) {
-    const moe::TileCfg small = mean <= 24 ? moe::TILE_STREAM_64 : moe::TILE_STREAM_192;
-    if (p->T <= 192) return {small, small, -1};
-    return {small, moe::TILE_MFMA, 192};
+    // decode-sized groups: the matrix-core GEMM's direct-to-LDS weight ring streams the
+    // weights faster than the register ring (measured 5.7 vs 5.5 TB/s on the gate_up of a
+    // 64-token batch), and a group's partly filled tile costs only its 64-row blocks
+    if (mean <= 24) return {moe::TILE_MFMA, moe::TILE_MFMA, -1};
+    if (p->T <= 192) return {moe::TILE_STREAM_192, moe::TILE_STREAM_192, -1};
+    return {moe::TILE_STREAM_192, moe::TILE_MFMA, 192};
   }
   const moe::TileCfg c = mean <= 48 ? moe::TILE_SMALL : moe::TILE_LARGE;
   return {c, c, -1};
