@@ -442,7 +442,7 @@ const char* moe_describe_plan(const moe_problem* p) {
           ? "split-K mfma 16x64, " + std::to_string(router_ks(p)) + " K slice(s)"
           : name(dense_cfg(p->T, p->E + (gated(p) ? 1 : 0)));
   text = "router: " + router + "; dispatch: " +
-         (moe::dispatch_fused(p->T * p->K, p->E) ? "one work-group" : "count/scan/scatter") +
+         (moe::dispatch_fused(p->T * p->K, p->E) ? "one work-group" : "count, then scan+scatter") +
          "; grouped gate_up/down: " + name(grouped_plan(p).cfg0);
   if (grouped_plan(p).split >= 0)
     text += " (experts with <= " + std::to_string(grouped_plan(p).split) + " rows), " +

@@ -5,17 +5,15 @@
 //
 // The assignments a = t*K + k are cut into segments of 1024 consecutive ids, one wave64 each
 // (each lane prefetches its 16 ids of the segment at once).
-//   count   : each wave histograms its segment in LDS (atomics are fine: counts do not depend
-//             on order) and writes seg_counts[segment][E].
-//   scan    : one work-group scans seg_counts expert-major (expert, then segment), giving every
-//             (segment, expert) pair its first output position, the expert counts and offsets,
-//             and the grouped-GEMM tile map.
-//   scatter : each wave re-reads its segment 64 ids at a time.  Lanes holding the same expert
-//             find each other with one ballot per bit of the expert id; a lane's rank among its
-//             lower-numbered peers plus the running rank of its expert (in LDS) is its rank
-//             q within the expert, and offsets[e] + q its output position.  Segments, rounds
-//             and lanes all follow ascending a, so the sort is stable and the result
-//             bit-exact.
+//   count        : each wave histograms its segment in LDS (atomics are fine: counts do not
+//                  depend on order) and writes seg_counts[segment][E].
+//   scan_scatter : every work-group re-derives the expert totals, offsets and its segments'
+//                  first ranks from seg_counts (work-group 0 also writes counts, offsets and
+//                  the tile maps); then each wave re-reads its segment 64 ids at a time and
+//                  places every assignment by its ballot-computed rank.  Segments, rounds and
+//                  lanes all follow ascending a, so the sort is stable and the result
+//                  bit-exact.
+// Small batches take one work-group for the whole dispatch (dispatch_fused_kernel).
 // Expert capacity ("1.6 混合专家（MoE）" §三): with a cap C, scan counts min(t_e, C) rows per
 // expert (so offsets and tile maps cover only kept rows) and scatter drops every assignment
 // whose rank q is C or more (inv_perm = -1): each expert keeps its first C assignments.
@@ -44,25 +42,26 @@ __device__ __forceinline__ int wave_prefix_exclusive(int v, int lane) {
   return x - v;
 }
 
-// Exclusive scan of one int per thread across a 1024-thread block.  Returns the prefix and
+// Exclusive scan of one int per thread across an NT-thread block.  Returns the prefix and
 // writes the block total to *total.
-__device__ int block_exclusive_scan(int v, int* scratch /* >= 17 ints */, int* total) {
+template <int NT>
+__device__ int block_exclusive_scan(int v, int* scratch /* >= NT / 64 + 1 ints */, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ex = wave_prefix_exclusive(v, lane);
   if (lane == 63) scratch[wave] = ex + v;
   __syncthreads();
   if (threadIdx.x == 0) {
     int run = 0;
-    for (int w = 0; w < kScanThreads / 64; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
       const int c = scratch[w];
       scratch[w] = run;
       run += c;
     }
-    scratch[kScanThreads / 64] = run;
+    scratch[NT / 64] = run;
   }
   __syncthreads();
   const int r = ex + scratch[wave];
-  *total = scratch[kScanThreads / 64];
+  *total = scratch[NT / 64];
   __syncthreads();
   return r;
 }
@@ -100,12 +99,13 @@ __global__ void __launch_bounds__(256) count_kernel(const int32_t* __restrict__ 
 // row more): its tiles then cost the same, run in step on one XCD and fetch each weight tile
 // once into its L2 for all of them (a full tile and a short last one drift apart, and each
 // streams the weights from memory by itself).
+template <int NT>
 __device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, const TileSplit ts,
                             int* scratch, int32_t* tiles, int32_t* tile_count) {
   int32_t* maps[2] = {tiles, tiles + ts.map1_entries * kTileStride};
   const int bms[2] = {ts.bm0, ts.bm1};
   int total[2] = {0, 0};
-  for (int base = 0; base < E; base += kScanThreads) {
+  for (int base = 0; base < E; base += NT) {
     const int e = base + threadIdx.x;
     const int c = e < E ? cnt_lds[e] : 0;
     const int which = (ts.split >= 0 && c > ts.split) ? 1 : 0;
@@ -114,7 +114,7 @@ __device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, const
       const int bm = bms[m];
       const int mt = which == m ? (c + bm - 1) / bm : 0;
       int chunk_total;
-      const int first = block_exclusive_scan(mt, scratch, &chunk_total) + total[m];
+      const int first = block_exclusive_scan<NT>(mt, scratch, &chunk_total) + total[m];
       const int base_rows = mt > 0 ? c / mt : 0, extra = mt > 0 ? c % mt : 0;
       for (int q = 0; q < mt; ++q) {
         int32_t* ent = maps[m] + (int64_t)(first + q) * kTileStride;
@@ -136,73 +136,6 @@ __device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, const
   }
 }
 
-__global__ void __launch_bounds__(kScanThreads) scan_kernel(int32_t* __restrict__ seg_counts,
-                                                            int64_t nseg, int E, int cap,
-                                                            int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ offsets,
-                                                            const TileSplit ts,
-                                                            int32_t* __restrict__ tiles,
-                                                            int32_t* __restrict__ tile_count) {
-  extern __shared__ int sm[];
-  int* cnt = sm;             // [E]
-  int* off = sm + E;         // [E]
-  int* part = sm + 2 * E;    // [kScanThreads]
-  int* scratch = part + kScanThreads;  // [17]
-  // Threads are (chunk c, expert e); P chunks per expert split the segments.  E <= 1024.
-  int ep = 1;
-  while (ep < E) ep <<= 1;
-  const int P = kScanThreads / ep;
-  const int e = threadIdx.x % ep, c = threadIdx.x / ep;
-  const int64_t per = (nseg + P - 1) / P;
-  const int64_t s0 = (int64_t)c * per, s1 = min(nseg, s0 + per);
-  const bool active = e < E;
-  int sum = 0;
-  if (active) {
-    for (int64_t s = s0; s < s1; s += 16) {
-      int v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = s + u < s1 ? seg_counts[(s + u) * E + e] : 0;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) sum += v[u];
-    }
-  }
-  part[threadIdx.x] = sum;
-  __syncthreads();
-  if (active) {
-    int run = 0;
-    for (int cc = 0; cc < c; ++cc) run += part[cc * ep + e];
-    for (int64_t s = s0; s < s1; s += 16) {
-      int v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = s + u < s1 ? seg_counts[(s + u) * E + e] : 0;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (s + u < s1) seg_counts[(s + u) * E + e] = run;  // the segment's first rank in e
-        run += v[u];
-      }
-    }
-    if (c == P - 1) cnt[e] = run < cap ? run : cap;  // rows kept
-  }
-  __syncthreads();
-  // expert offsets
-  int total = 0;
-  for (int base = 0; base < E; base += kScanThreads) {
-    const int ee = base + threadIdx.x;
-    const int v = ee < E ? cnt[ee] : 0;
-    int chunk_total;
-    const int ex = block_exclusive_scan(v, scratch, &chunk_total) + total;
-    if (ee < E) {
-      off[ee] = ex;
-      counts[ee] = v;
-      offsets[ee] = ex;
-    }
-    total += chunk_total;
-  }
-  if (threadIdx.x == 0) offsets[E] = total;
-  __syncthreads();
-  if (tiles) build_tiles(cnt, off, E, ts, scratch, tiles, tile_count);
-}
-
 __global__ void __launch_bounds__(kScanThreads) tile_map_kernel(const int32_t* __restrict__ offsets,
                                                                 int E, const TileSplit ts,
                                                                 int32_t* __restrict__ tiles,
@@ -216,49 +149,94 @@ __global__ void __launch_bounds__(kScanThreads) tile_map_kernel(const int32_t* _
     cnt[e] = offsets[e + 1] - offsets[e];
   }
   __syncthreads();
-  build_tiles(cnt, off, E, ts, scratch, tiles, tile_count);
+  build_tiles<kScanThreads>(cnt, off, E, ts, scratch, tiles, tile_count);
 }
 
-__global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ idx, int64_t A,
-                                                      int E, int nbits, int cap, int64_t nseg,
-                                                      const int32_t* __restrict__ seg_base,
-                                                      const int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ perm,
-                                                      int32_t* __restrict__ inv_perm) {
-  extern __shared__ int run_all[];
+// Scan and scatter in one launch.  Work-group b owns segments [8 b, 8 b + 8), one per wave.
+// Every work-group first re-derives, from the per-segment histograms, each expert's total
+// (capped at the capacity) and the first rank of its own segments within the expert; the
+// histograms are a few KiB per hundred segments, read from L2.  Work-group 0 also writes the
+// counts, offsets and tile maps.  Then each wave re-reads its segment 64 ids at a time: lanes
+// holding the same expert find each other with one ballot per bit of the expert id, and a
+// lane's rank among its lower-numbered peers plus its expert's running rank (in LDS) is its
+// rank q within the expert; offsets[e] + q is its position, unless q reaches the capacity.
+constexpr int kSSThreads = 512;
+constexpr int kSSWaves = kSSThreads / 64;
+constexpr int kSSBatch = 8;  // histogram rows loaded together
+
+__global__ void __launch_bounds__(kSSThreads) scan_scatter_kernel(
+    const int32_t* __restrict__ idx, int64_t A, int E, int nbits, int cap, int64_t nseg,
+    const int32_t* __restrict__ seg_counts, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    const TileSplit ts, int32_t* __restrict__ tiles, int32_t* __restrict__ tile_count) {
+  extern __shared__ int sm[];
+  int* run = sm;                      // [kSSWaves][E]: next rank in each expert, per segment
+  int* cnt = run + kSSWaves * E;      // [E] rows kept
+  int* off = cnt + E;                 // [E]
+  int* scratch = off + E;             // [32]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t seg = (int64_t)blockIdx.x * 4 + wave;
-  if (seg >= nseg) return;
-  int* run = run_all + wave * 2 * E;  // next rank within each expert
-  int* off = run + E;                  // expert offsets
+  const int64_t seg0 = (int64_t)blockIdx.x * kSSWaves;
+
+  for (int e = threadIdx.x; e < E; e += kSSThreads) {
+    int acc = 0;
+    for (int64_t s0 = 0; s0 < nseg; s0 += kSSBatch) {
+      int v[kSSBatch];
+#pragma unroll
+      for (int u = 0; u < kSSBatch; ++u) v[u] = s0 + u < nseg ? seg_counts[(s0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kSSBatch; ++u) {
+        const int64_t sg = s0 + u;
+        if (sg >= seg0 && sg < seg0 + kSSWaves) run[(sg - seg0) * E + e] = acc;
+        acc += v[u];
+      }
+    }
+    cnt[e] = acc < cap ? acc : cap;
+  }
+  __syncthreads();
+  int total = 0;
+  for (int base = 0; base < E; base += kSSThreads) {
+    const int ee = base + threadIdx.x;
+    const int v = ee < E ? cnt[ee] : 0;
+    int chunk_total;
+    const int ex = block_exclusive_scan<kSSThreads>(v, scratch, &chunk_total) + total;
+    if (ee < E) {
+      off[ee] = ex;
+      if (blockIdx.x == 0) {
+        counts[ee] = v;
+        offsets[ee] = ex;
+      }
+    }
+    total += chunk_total;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) offsets[E] = total;
+  __syncthreads();
+  if (blockIdx.x == 0 && tiles) build_tiles<kSSThreads>(cnt, off, E, ts, scratch, tiles, tile_count);
+
+  const int64_t seg = seg0 + wave;
+  if (seg >= nseg) return;  // after every work-group barrier
+  int* r = run + wave * E;
   const int64_t a0 = seg * kSegLen;
   int ev[kSegRounds];
 #pragma unroll
-  for (int r = 0; r < kSegRounds; ++r) {
-    const int64_t a = a0 + r * 64 + lane;
-    ev[r] = a < A ? idx[a] : -1;
+  for (int rd = 0; rd < kSegRounds; ++rd) {
+    const int64_t a = a0 + rd * 64 + lane;
+    ev[rd] = a < A ? idx[a] : -1;
   }
-  for (int e = lane; e < E; e += 64) {
-    run[e] = seg_base[seg * E + e];
-    off[e] = offsets[e];
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
-  for (int r = 0; r < kSegRounds; ++r) {
-    const int64_t a = a0 + r * 64 + lane;
-    const int e = ev[r];
+  for (int rd = 0; rd < kSegRounds; ++rd) {
+    const int64_t a = a0 + rd * 64 + lane;
+    const int e = ev[rd];
     const bool valid = e >= 0 && e < E;
     unsigned long long peers = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
+    for (int bt = 0; bt < nbits; ++bt) {
+      const bool bit = (e >> bt) & 1;
       const unsigned long long m = __ballot(bit);
       peers &= bit ? m : ~m;
     }
     if (valid) {
       const int rank = __popcll(peers & lt);
-      const int base = run[e];
+      const int base = r[e];
       const int q = base + rank;  // rank of this assignment within its expert
       if (q < cap) {
         const int pos = off[e] + q;
@@ -267,7 +245,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
       } else {
         inv_perm[a] = -1;  // over capacity: dropped
       }
-      if (rank == 0) run[e] = base + __popcll(peers);
+      if (rank == 0) r[e] = base + __popcll(peers);
     } else if (a < A) {
       inv_perm[a] = -1;
     }
@@ -279,7 +257,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
 // Whole dispatch in one work-group, for batches whose launch latency would otherwise dominate:
 // wave w owns the contiguous range [w*L, (w+1)*L) of assignment ids.  Count (LDS atomics into
 // the wave's own histogram), exclusive prefix over waves per expert, expert offsets, tile maps,
-// then the same ballot-ranked stable scatter as scatter_kernel.  Wave ranges, rounds and lanes
+// then the same ballot-ranked stable scatter as scan_scatter_kernel.  Wave ranges, rounds and lanes
 // all follow ascending a, so the result equals the multi-kernel path's bit for bit.
 constexpr int kFusedWaves = kScanThreads / 64;
 constexpr int kFusedBatch = 8;  // 64-id rounds whose loads are issued together
@@ -329,7 +307,7 @@ __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
     const int ee = base + threadIdx.x;
     const int v = ee < E ? cnt[ee] : 0;
     int chunk_total;
-    const int ex = block_exclusive_scan(v, scratch, &chunk_total) + total;
+    const int ex = block_exclusive_scan<kScanThreads>(v, scratch, &chunk_total) + total;
     if (ee < E) {
       off[ee] = ex;
       counts[ee] = v;
@@ -339,7 +317,7 @@ __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
   }
   if (threadIdx.x == 0) offsets[E] = total;
   __syncthreads();
-  if (tiles) build_tiles(cnt, off, E, ts, scratch, tiles, tile_count);
+  if (tiles) build_tiles<kScanThreads>(cnt, off, E, ts, scratch, tiles, tile_count);
   __syncthreads();
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t b0 = a_begin; b0 < a_end; b0 += 64 * kFusedBatch) {
@@ -425,17 +403,14 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_co
     return hipGetLastError();
   }
   const dim3 g((unsigned)((nseg + 3) / 4)), b(256);
-  const size_t lds_waves = (size_t)4 * E * sizeof(int);
-  hipLaunchKernelGGL(count_kernel, g, b, lds_waves, stream, idx, A, E, nseg, seg_counts);
+  hipLaunchKernelGGL(count_kernel, g, b, (size_t)4 * E * sizeof(int), stream, idx, A, E, nseg,
+                     seg_counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const size_t lds_scan = (size_t)(2 * E + kScanThreads + 32) * sizeof(int);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), lds_scan, stream, seg_counts, nseg,
-                     E, cap, counts, offsets, ts, tiles, tile_count);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(scatter_kernel, g, b, 2 * lds_waves, stream, idx, A, E, nbits, cap, nseg,
-                     seg_counts, offsets, perm, inv_perm);
+  const size_t lds = (size_t)((kSSWaves + 2) * E + 32) * sizeof(int);
+  hipLaunchKernelGGL(scan_scatter_kernel, dim3((unsigned)((nseg + kSSWaves - 1) / kSSWaves)),
+                     dim3(kSSThreads), lds, stream, idx, A, E, nbits, cap, nseg, seg_counts,
+                     counts, offsets, perm, inv_perm, ts, tiles, tile_count);
   return hipGetLastError();
 }
 
