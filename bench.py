@@ -48,6 +48,9 @@ def parse_args():
     ap.add_argument("--decode-workload", default="a3b_decode")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mfma-workload", default="ds_sigmoid",
+                    help="matrix-core-bound workload reported beside the main one")
+    ap.add_argument("--no-mfma-workload", action="store_true")
     ap.add_argument("--no-granularity", action="store_true",
                     help="skip the granularity pair (128 experts x F=1536 x top-8 vs "
                          "64 x 3072 x top-4)")
@@ -259,6 +262,22 @@ def main():
                                     args.atomic_combine, hip)
         sys.stderr.write(json.dumps({"progress": "decode workload timed",
                                      "ms_per_step": decode["ms_per_step"]}) + "\n")
+    mfma_bound = None
+    if not args.no_mfma_workload and args.mfma_workload != args.workload:
+        g, lay, _ = run_workload(args.mfma_workload, args.steps, args.warmup, args.atomic_combine,
+                                 hip)
+        del lay
+        torch.cuda.empty_cache()
+        pk = costmodel.MFMA_BF16_PEAK_TFLOPS
+        mfma_bound = {
+            "workload": args.mfma_workload, "plan": g["plan"], "T": g["T"], "U": g["U"],
+            "t_e": g["t_e"], "ms_per_step": g["ms_per_step"], "tokens_per_s": g["tokens_per_s"],
+            "gate_up_tflops": g["gate_up"]["tflops"], "gate_up_mfma_frac": g["gate_up"]["tflops"] / pk,
+            "down_tflops": g["down"]["tflops"], "down_mfma_frac": g["down"]["tflops"] / pk,
+            "layer_tflops": g["layer_tflops"], "layer_mfma_frac": g["layer_tflops"] / pk,
+            "stage_ms": g["stage_ms"]}
+        sys.stderr.write(json.dumps({"progress": f"{args.mfma_workload} timed",
+                                     "ms_per_step": g["ms_per_step"]}) + "\n")
     granularity = None
     if not args.no_granularity:
         from mixture_experts_layer_renorm_amd.synth import GRANULARITY_PAIR
@@ -318,6 +337,7 @@ def main():
             "expert_weight_gbs": decode["expert_weight_gbs"],
             "expert_weight_hbm_frac": decode["expert_weight_gbs"] / costmodel.HBM_PEAK_GBS,
             "stage_ms": decode["stage_ms"]},
+        "mfma_bound": mfma_bound,
         "granularity": granularity,
     }
     print(json.dumps(line))
