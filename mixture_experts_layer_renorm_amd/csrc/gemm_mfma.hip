@@ -112,16 +112,27 @@ constexpr int kNW = 8;                 // waves: 4 along M x 2 along N
 constexpr int kNT = 64 * kNW;          // threads
 constexpr int kDma = kBM / 8 / kNW;    // 1 KiB DMA instructions per wave per full operand stage
 
-// One output tile.  Wave (wm, wn) owns rows [16 MIA wm, +16 MIA) and columns [128 wn, +128) as
-// MIA x 8 MFMA tiles of 16 x 16; a tile of `rows` rows runs with MIA = ceil(rows / 64), so a
-// partly filled tile (a group's last one) costs MIA/4 of a full one: the two waves that share
-// a SIMD own different row blocks, and only the token rows [0, 64 MIA) are fetched.
-template <int MIA, int EPI>
+// First row of wave row block wm when blocks 0 and 1 hold mi_hi and blocks 2 and 3 mi_lo
+// 16-row MFMA tiles.
+__device__ __forceinline__ int block_row0(int wm, int mi_hi, int mi_lo) {
+  return wm < 2 ? wm * 16 * mi_hi : 32 * mi_hi + (wm - 2) * 16 * mi_lo;
+}
+
+// One output tile.  Wave (wm, wn) owns MI x 8 MFMA tiles of 16 x 16: columns [128 wn, +128)
+// and MI 16-row tiles starting at block_row0(wm).  A tile of `rows` rows is computed as
+// P = ceil(rows / 32) pairs of 16-row tiles: row blocks 0 and 1 take mi_hi = ceil(P / 2) each,
+// blocks 2 and 3 mi_lo = floor(P / 2).  The two waves that share a SIMD (waves w and w + 4)
+// hold one block of each kind, so every SIMD runs P sets of 8 MFMAs per K step and a partly
+// filled tile (a group's last one) costs in proportion to its rows, to 32 rows.  Only the
+// token rows [0, 32 P) are fetched; MI is also this wave's count of 1 KiB token-row DMA
+// instructions per stage.
+template <int MI, int EPI>
 __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int tid, int wave,
                                           int group, int row_start, int rows, int n_tile,
-                                          int ns) {
+                                          int ns, int mi_hi, int mi_lo) {
   constexpr bool kSwiglu = EPI == EPI_SWIGLU;
-  static_assert(MIA >= 1 && MIA <= 4 && kDma == 4 && 4 * kDma < 64, "tile shape, vmcnt range");
+  constexpr int MIA = MI > 0 ? MI : 1;  // array extent
+  static_assert(MI >= 0 && MI <= 4 && kDma == 4 && 4 * kDma < 64, "tile shape, vmcnt range");
   char* const sA = smem;                  // token-row ring, kSA stages
   char* const sB = smem + kSA * kAStage;  // weight ring, kSB stages
   const int lane = tid & 63;
@@ -131,7 +142,8 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
   // Lane offsets (within a stage) of this wave's first A and B fragment rows, for each 32-wide
   // half of the stage.  For SwiGLU the tile's first 128 B rows are gate rows and the next 128
   // the matching up rows, and a wave's column tiles j and j + 4 are a gate/up pair.
-  const int la_row = (wm * MIA * 16 + lr) * kRow;
+  const int wrow0 = block_row0(wm, mi_hi, mi_lo);
+  const int la_row = (wrow0 + lr) * kRow;
   const int lb_row = ((kSwiglu ? wn * 64 : wn * 128) + lr) * kRow;
   const int ch0 = (lk ^ swz(lr)) << 4, ch1 = ((4 + lk) ^ swz(lr)) << 4;
 
@@ -158,7 +170,7 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
 
   f32x4 acc[MIA][8];
 #pragma unroll
-  for (int i = 0; i < MIA; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -166,12 +178,12 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
   barrier_after<0, 0>();
   // Ring schedule (per wave, in issue order): prologue A0 B0 A1 B1 B2, then before stage g+1
   // is used, A(g+2) B(g+3).  Token rows run two stages ahead, weights three, so up to 64 KiB
-  // of weights per CU are in flight.  A stage of token rows is MIA instructions per wave, one
+  // of weights per CU are in flight.  A stage of token rows is MI instructions per wave, one
   // of weights kDma; the waits below count exactly those.
-  dma_operand<kNW, MIA>(p.A, srcA, 0, sA, wave);
+  dma_operand<kNW, MI>(p.A, srcA, 0, sA, wave);
   dma_operand<kNW>(gbase, srcB, 0, sB, wave);
   if (ns > 1) {
-    dma_operand<kNW, MIA>(p.A, srcA, kRow, sA + kAStage, wave);
+    dma_operand<kNW, MI>(p.A, srcA, kRow, sA + kAStage, wave);
     dma_operand<kNW>(gbase, srcB, kRow, sB + kBStage, wave);
   }
   if (ns > 2) dma_operand<kNW>(gbase, srcB, 2 * kRow, sB + 2 * kBStage, wave);
@@ -180,10 +192,10 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
   // B fragments alternate between two sets)
   bf16x8 af0[MIA], bf0[8], bf1[8];
   if (ns > 2)  // A1 B1 B2 were issued after B0 and may still fly
-    barrier_after<MIA + 2 * kDma, 0>();
+    barrier_after<MI + 2 * kDma, 0>();
   else
     barrier_after<0, 0>();
-  read_frags<MIA, kSwiglu>(sA + la_row + ch0, sB + lb_row + ch0, af0, bf0);
+  if constexpr (MI > 0) read_frags<MI, kSwiglu>(sA + la_row + ch0, sB + lb_row + ch0, af0, bf0);
 
   // Stage g's MFMAs: first half (step 2g) while reading the second half's fragments from
   // the same stage; then publish stage g+1 (this wave's copies landed; every wave has read
@@ -192,29 +204,30 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
   for (int g = 0; g < ns; ++g) {
     const char* ca = sA + (g % kSA) * kAStage;
     const char* cb = sB + (g % kSB) * kBStage;
-    mma_stage<MIA, kSwiglu>(acc, af0, bf0, ca + la_row + ch1, cb + lb_row + ch1, bf1);
+    if constexpr (MI > 0)
+      mma_stage<MI, kSwiglu>(acc, af0, bf0, ca + la_row + ch1, cb + lb_row + ch1, bf1);
     if (g + 1 < ns) {
       if (g + 2 < ns)  // B(g+2) went out after A(g+1) and may still fly
         barrier_after<kDma, 0>();
       else
         barrier_after<0, 0>();
       if (g + 2 < ns)
-        dma_operand<kNW, MIA>(p.A, srcA, (uint32_t)(g + 2) * kRow, sA + (g % kSA) * kAStage,
-                              wave);
+        dma_operand<kNW, MI>(p.A, srcA, (uint32_t)(g + 2) * kRow, sA + (g % kSA) * kAStage,
+                             wave);
       if (g + 3 < ns)
         dma_operand<kNW>(gbase, srcB, (uint32_t)(g + 3) * kRow, sB + (g % kSB) * kBStage, wave);
     }
     // after the last stage these reads fetch unused leftovers
     const char* na = sA + ((g + 1) % kSA) * kAStage;
     const char* nb = sB + ((g + 1) % kSB) * kBStage;
-    mma_stage<MIA, kSwiglu>(acc, af0, bf1, na + la_row + ch0, nb + lb_row + ch0, bf0);
+    if constexpr (MI > 0)
+      mma_stage<MI, kSwiglu>(acc, af0, bf1, na + la_row + ch0, nb + lb_row + ch0, bf0);
   }
 
   // ---- epilogue (staged in the ring's LDS) ---------------------------------------------------
-  // Lane (lr, lk) holds rows 16 (MIA wm + i) + 4 lk + r of column tile j in acc[i][j][r].  The
+  // Lane (lr, lk) holds rows wrow0 + 16 i + 4 lk + r of column tile j in acc[i][j][r].  The
   // thread index is laundered through an empty asm so the store offsets below are computed
   // here, not hoisted out of the tile loop into registers (and spilled).
-  constexpr int kWaveRows = MIA * 16;  // rows per wave row block
   int etid = tid;
   asm volatile("" : "+v"(etid));
   const int elr = etid & 15, elk = (etid >> 4) & 3;
@@ -224,12 +237,12 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
     constexpr int kLdH = kBN / 2 + 8;
     __bf16* Eh = (__bf16*)smem;
 #pragma unroll
-    for (int i = 0; i < MIA; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = wm * kWaveRows + i * 16 + elk * 4 + r;
+          const int row = wrow0 + i * 16 + elk * 4 + r;
           const int col = wn * 64 + j * 16 + elr;
           Eh[row * kLdH + col] = (__bf16)(silu_fast(acc[i][j][r]) * acc[i][j + 4][r]);
         }
@@ -237,8 +250,8 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
     constexpr int kCpr = kBN / 2 / 8;  // 16 chunks of 8 values per H row
     char* Ht = (char*)p.C + ((int64_t)row_start * p.ldc + n_tile * (kBN / 2)) * 2;
     const int ncols = min(kBN / 2, p.N - n_tile * (kBN / 2));
-#pragma unroll
-    for (int mm = 0; mm < 4 * kWaveRows * kCpr / kNT; ++mm) {
+    const int nmm = (rows * kCpr + kNT - 1) / kNT;
+    for (int mm = 0; mm < nmm; ++mm) {
       const int c = etid + kNT * mm;
       const int row = c / kCpr, ch = c % kCpr;
       if (row < rows && ch * 8 < ncols)
@@ -257,7 +270,7 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
       float* tmax = (float*)(smem + kLds - 64);
       float mx = 0.0f;
 #pragma unroll
-      for (int i = 0; i < MIA; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -277,10 +290,12 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
     constexpr int kCpr = kBN / 4;  // 16-byte chunks per fp32 row
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
-      if (pass * kWaveRows < rows) {  // uniform
+      const int prow0 = block_row0(pass, mi_hi, mi_lo);
+      const int pmi = pass < 2 ? mi_hi : mi_lo;
+      if (pmi > 0 && prow0 < rows) {  // uniform
         if (wm == pass) {
 #pragma unroll
-          for (int i = 0; i < MIA; ++i)
+          for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -288,11 +303,10 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
                 E[(i * 16 + elk * 4 + r) * kLdE + wn * 128 + j * 16 + elr] = acc[i][j][r];
         }
         barrier_after<0, 0>();
-#pragma unroll
-        for (int mm = 0; mm < kWaveRows * kCpr / kNT; ++mm) {
+        for (int mm = 0; mm < 2 * pmi; ++mm) {  // 16 pmi rows of kCpr chunks
           const int c = etid + kNT * mm;
           const int lrow = c / kCpr, col = (c % kCpr) * 4;  // one row per wave
-          const int row = pass * kWaveRows + lrow;
+          const int row = prow0 + lrow;
           if (p.c_scale) {
             // fp16 with the tile's power-of-two factor
             const f32x4 v = *(const f32x4*)(E + lrow * kLdE + col);
@@ -315,10 +329,10 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
     }
   } else {  // EPI_ATOMIC_COMBINE
 #pragma unroll
-    for (int i = 0; i < MIA; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = wm * kWaveRows + i * 16 + elk * 4 + r;
+        const int row = wrow0 + i * 16 + elk * 4 + r;
         if (row >= rows) continue;
         const int a = p.perm[row_start + row];
         const float w = p.topk_w[a];
@@ -364,18 +378,24 @@ mfma_kernel(const GemmParams p) {
       row_start = load_uniform(p.tiles, m * kTileStride + 1);
       rows = load_uniform(p.tiles, m * kTileStride + 2);
     }
-    switch ((rows + 63) >> 6) {  // 16-row MFMA tiles per wave that hold rows
+    // 32-row pairs of MFMA row tiles that hold rows, split over the wave row blocks
+    const int pairs = min(max((rows + 31) >> 5, 1), 8);
+    const int mi_hi = (pairs + 1) >> 1, mi_lo = pairs >> 1;
+    switch (wave < 4 ? mi_hi : mi_lo) {  // waves 0-3 hold row blocks 0 and 1
+      case 0:
+        mfma_tile<0, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns, mi_hi, mi_lo);
+        break;
       case 1:
-        mfma_tile<1, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns);
+        mfma_tile<1, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns, mi_hi, mi_lo);
         break;
       case 2:
-        mfma_tile<2, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns);
+        mfma_tile<2, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns, mi_hi, mi_lo);
         break;
       case 3:
-        mfma_tile<3, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns);
+        mfma_tile<3, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns, mi_hi, mi_lo);
         break;
       default:
-        mfma_tile<4, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns);
+        mfma_tile<4, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns, mi_hi, mi_lo);
         break;
     }
   }

@@ -168,7 +168,7 @@ GROUPED_TILES = ["small", "large", "stream64", "stream128", "stream192", "mfma"]
 
 @pytest.mark.parametrize("tile", GROUPED_TILES)
 @pytest.mark.parametrize("name", ["a3b_E16", "a17b_E32", "skew_conc_E64", "ds_sigmoid_E16",
-                                  "a3b_T1", "odd_k"])
+                                  "a3b_T1", "odd_k", "skew_E64"])
 def test_every_grouped_tile_shape_matches_oracle(name, tile, monkeypatch):
     """The library picks the grouped GEMM's tile from the mean rows per expert; forcing each
     shape on the same inputs covers ragged groups, multi-tile experts and empty experts in all."""
