@@ -119,17 +119,16 @@ GroupedPlan grouped_plan(const moe_problem* p) {
     if (bf && !std::strcmp(o, "stream192"))
       return {moe::TILE_STREAM_192, moe::TILE_STREAM_192, -1};
     if (bf && !std::strcmp(o, "mfma")) return {moe::TILE_MFMA, moe::TILE_MFMA, -1};
+    if (bf && !std::strcmp(o, "split192"))  // streaming GEMM up to 192 rows, matrix-core above
+      return {moe::TILE_STREAM_192, moe::TILE_MFMA, 192};
   }
-  const int64_t A = p->T * p->K;
-  const double mean = (double)A / p->E;
-  if (bf) {
-    // decode-sized groups: the matrix-core GEMM's direct-to-LDS weight ring streams the
-    // weights faster than the register ring (measured 5.7 vs 5.5 TB/s on the gate_up of a
-    // 64-token batch), and a group's partly filled tile costs only its 64-row blocks
-    if (mean <= 24) return {moe::TILE_MFMA, moe::TILE_MFMA, -1};
-    if (p->T <= 192) return {moe::TILE_STREAM_192, moe::TILE_STREAM_192, -1};
-    return {moe::TILE_STREAM_192, moe::TILE_MFMA, 192};
-  }
+  // bf16: the matrix-core GEMM for every group size.  Its direct-to-LDS weight ring streams
+  // the weights faster than the register ring of the streaming GEMM (5.7 vs 5.5 TB/s on the
+  // gate_up of a 64-token batch), and a group's partly filled tile costs only its 32-row
+  // blocks, where the streaming GEMM runs all of its 192 rows (a 4096-token 35B-A3B-shaped
+  // layer: gate_up 221 vs 231 us; a 8192-token 397B-A17B-shaped one: 1706 vs 1882 us).
+  if (bf) return {moe::TILE_MFMA, moe::TILE_MFMA, -1};
+  const double mean = (double)(p->T * p->K) / p->E;
   const moe::TileCfg c = mean <= 48 ? moe::TILE_SMALL : moe::TILE_LARGE;
   return {c, c, -1};
 }

@@ -163,7 +163,7 @@ def test_concentrated_routing_hits_eight_experts():
     assert np.all(counts[hot_experts(cfg)] == T)
 
 
-GROUPED_TILES = ["small", "large", "stream64", "stream128", "stream192", "mfma"]
+GROUPED_TILES = ["small", "large", "stream64", "stream128", "stream192", "mfma", "split192"]
 
 
 @pytest.mark.parametrize("tile", GROUPED_TILES)
