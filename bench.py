@@ -26,10 +26,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PROFILES = os.path.join(ROOT, "profiles")
-# sources the grouped streaming GEMM is compiled from (a traffic record is only used if it was
+# sources the grouped matrix-core GEMM is compiled from (a traffic record is only used if it was
 # taken on exactly these)
 _CSRC = os.path.join(ROOT, "mixture_experts_layer_renorm_amd", "csrc")
-GEMM_SRCS = [os.path.join(_CSRC, f) for f in ("gemm_stream.hip", "kernels.h", "silu.h")]
+GEMM_SRCS = [os.path.join(_CSRC, f) for f in ("gemm_mfma.hip", "kernels.h", "silu.h")]
 
 
 def gemm_source_sha256() -> str:
