@@ -83,19 +83,17 @@ int32_t capacity(const moe_problem* p) {
 }
 bool gated(const moe_problem* p) { return p->F_shared > 0 && p->shared_gated; }
 
-// Grouped (routed-expert) GEMMs.  The host does not see the per-expert counts (no sync), so the
-// dispatch kernel sorts the experts into two tile maps on the device: experts with up to 192
-// rows are bound by reading their weights and go to the weight-streaming GEMM (192-row M
-// tiles); larger groups reuse each weight byte hundreds of times and go to the matrix-core GEMM
-// (256 x 256 tiles).  Decode-sized batches (mean group <= 24 rows) run every group on the
-// matrix-core GEMM.  No expert can have
-// more than T rows, so for T <= 192 the second map is not built.  fp32 layers (and operands
-// of 4 GiB or more) use the tile GEMM with one map.  MOE_GROUPED_TILE (small, large, stream64,
-// stream128, stream192, mfma) forces one map with the named tile, for tuning and for tests
-// that cover every tile shape at small sizes; the streaming and MFMA shapes apply to bf16 only.
-// The streaming and matrix-core GEMMs address their operands with 32-bit offsets from a
-// uniform base: token rows ([T*K, max(D, F)] at most, via x_perm or H) and one expert's weights
-// must each span less than 4 GiB.
+// Grouped (routed-expert) GEMMs.  bf16 layers run every expert group on the matrix-core GEMM
+// (256 x 256 tiles, a partial tile computed in 32-row steps), one tile map of up to 256-row M
+// tiles.  fp32 layers (and operands of 4 GiB or more) use the tile GEMM with one map.
+// MOE_GROUPED_TILE overrides the plan for tuning and for the tests that cover every kernel at
+// small sizes: small, large, stream64, stream128, stream192 and mfma force one map with the
+// named tile; split192 puts experts with up to 192 rows on the weight-streaming GEMM and the
+// larger ones on the matrix-core GEMM, in two maps that the dispatch kernel fills on the
+// device (the host does not see the per-expert counts).  The streaming and MFMA shapes apply
+// to bf16 only.  The streaming and matrix-core GEMMs address their operands with 32-bit
+// offsets from a uniform base: token rows ([T*K, max(D, F)] at most, via x_perm or H) and one
+// expert's weights must each span less than 4 GiB.
 bool stream_fits(const moe_problem* p) {
   const int64_t es = (int64_t)esize(p->dtype);
   const int64_t wide = p->D > p->F ? p->D : p->F;

@@ -1,12 +1,14 @@
-// Matrix-core-bound grouped / dense GEMM (gfx950, bf16) for large token groups: experts that
-// receive hundreds of rows or more, and the shared expert, which sees every token.  There a
-// tile's weights are reused by many rows ("S23-J10" §3: a group's intensity is about t_e FLOP
-// per weight byte), so the limit is the MFMA pipes, and the kernel is shaped to keep them fed:
-//  * 8 waves (two per SIMD) over a 256 x 256 output tile, 4 along M x 2 along N; each wave
-//    owns 64 x 128 as 4 x 8 MFMA tiles of 16 x 16 (v_mfma_f32_16x16x32_bf16).  Per 32-wide K
-//    step a wave reads 4 A and 8 B fragments (12 KiB of LDS) for 32 MFMAs.  A tile with fewer
-//    rows runs with fewer 16-row MFMA tiles per wave (64-row granularity), so a group's
-//    partly filled last tile costs in proportion to its rows.
+// Matrix-core grouped / dense GEMM (gfx950, bf16): every routed expert group of a bf16 layer,
+// and the shared expert, which sees every token.  Groups of hundreds of rows reuse each weight
+// byte that many times ("S23-J10" §3: a group's intensity is about t_e FLOP per weight byte),
+// so there the limit is the MFMA pipes; decode-sized groups are bound by streaming their
+// weights, which the direct-to-LDS weight ring does at HBM speed.  The kernel:
+//  * 8 waves (two per SIMD) over a 256 x 256 output tile, 4 row blocks x 2 column halves of
+//    128; each wave owns MI x 8 MFMA tiles of 16 x 16 (v_mfma_f32_16x16x32_bf16), MI <= 4.
+//    Per 32-wide K step a wave reads MI A and 8 B fragments from LDS for 8 MI MFMAs.  A tile
+//    of r rows is computed in P = ceil(r / 32) pairs of 16-row MFMA tiles spread so that every
+//    SIMD runs P sets of 8 MFMAs (see mfma_tile), so a partly filled tile costs in proportion
+//    to its rows, to 32 rows.
 //  * K advances 64 per stage (128 bytes of every row, so each row's line is requested once).
 //    Both operands move from L2/HBM straight into LDS with global_load_lds_dwordx4 (no staging
 //    registers), token rows in a 2-stage ring and weights, which stream from HBM, in a

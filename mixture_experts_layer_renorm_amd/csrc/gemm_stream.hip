@@ -1,4 +1,7 @@
-// Weight-streaming grouped GEMM for the routed experts (gfx950, bf16).
+// Weight-streaming grouped GEMM for the routed experts (gfx950, bf16).  It runs the groups of
+// up to 192 rows under the split plan and the forced streaming plans; the default bf16 plan
+// runs every group on the matrix-core GEMM (gemm_mfma.hip), which computes a partial tile in
+// 32-row steps where this kernel always runs its BM rows.
 //
 // At the token counts of the layer's workloads an expert sees a few to a few hundred rows, so
 // the expert GEMMs are bound by reading the weights from HBM (read volume b_W·N_e·U:

@@ -62,14 +62,14 @@ struct GemmParams {
   int32_t topk;             // ATOMIC: K (token = assignment id / K)
 };
 
-// Tile configurations.  BM x BN output tile, 256 threads (4 waves as WM x WN).
+// Tile configurations (BM x BN output tiles).
 enum TileCfg : int {
   TILE_SMALL = 0,       // tile GEMM, BM=32,  BN=128
   TILE_LARGE = 1,       // tile GEMM, BM=256, BN=128
-  TILE_STREAM_64 = 2,   // weight-streaming GEMM, BM=64 (decode-sized groups), bf16 only
+  TILE_STREAM_64 = 2,   // weight-streaming GEMM, BM=64, bf16 only
   TILE_STREAM_192 = 3,  // weight-streaming GEMM, BM=192, bf16 only
   TILE_STREAM_128 = 4,  // weight-streaming GEMM, BM=128, bf16 only
-  TILE_MFMA = 5,        // matrix-core-bound GEMM, 256 x 256 tiles, bf16 only, no B2 / col_bias
+  TILE_MFMA = 5,        // matrix-core GEMM, 256 x 256 tiles, bf16 only, no B2 / col_bias
 };
 int tile_bm(TileCfg cfg);
 int tile_bn(TileCfg cfg);
@@ -78,7 +78,7 @@ int tile_bn(TileCfg cfg);
 hipError_t launch_stream_gemm(TileCfg cfg, Epilogue epi, const GemmParams& p, int64_t max_mtiles,
                               hipStream_t stream);
 
-// Matrix-core-bound grouped or dense GEMM (256 x 256 tiles), bf16.
+// Matrix-core grouped or dense GEMM (256 x 256 tiles), bf16.
 hipError_t launch_mfma_gemm(Epilogue epi, const GemmParams& p, int64_t max_mtiles,
                             hipStream_t stream);
 
