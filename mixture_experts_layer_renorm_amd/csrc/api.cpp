@@ -285,6 +285,7 @@ hipError_t launch_grouped(const moe_problem* p, const GroupedPlan& plan, moe::Ep
                           int64_t max_mtiles, hipStream_t s) {
   g.tiles = tiles;
   g.tile_count = tile_count;
+  g.rows_bound = (int32_t)p->T;  // an expert receives at most one row per token
   hipError_t e = moe::launch_gemm(p->dtype, plan.cfg0, epi, g, max_mtiles, s);
   if (e != hipSuccess || plan.split < 0) return e;
   g.tiles = tiles + max_mtiles * moe::kTileStride;

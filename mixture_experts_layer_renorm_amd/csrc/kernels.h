@@ -44,6 +44,7 @@ struct GemmParams {
   const int32_t* tiles;
   const int32_t* tile_count;
   int32_t M;
+  int32_t rows_bound;       // map mode: an upper bound on any tile's rows, or <= 0 if unknown
   // Epilogue operands.
   void* C;                  // STORE: fp32 [rows, ldc] (or fp16 with c_scale); SWIGLU: dtype
   int64_t ldc;

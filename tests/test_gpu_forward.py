@@ -47,6 +47,12 @@ CASES = {
     # expert outputs far above the fp16 range (|y| ~ 1e5): the fp16 rows of the default path
     # carry a power-of-two factor per 256-column block, so nothing overflows
     "huge_values": ("tiny", {"dtype": "bf16", "std_expert": 4.0, "D": 320}, 200),
+    # batches of at most 64 tokens: reductions of exactly three K stages (the shortest that
+    # carries the rings into the next tile) and of five, ragged N tiles, tiles over 32 rows
+    "small_ragged": ("a3b_prefill", {"D": 192, "F": 320, "E": 4, "K": 2}, 61),
+    # T = 64 with about 32 rows per expert: consecutive tiles alternate between one and two
+    # 32-row halves
+    "small_E8_T64": ("a3b_prefill", {"E": 8, "K": 4}, 64),
 }
 
 
