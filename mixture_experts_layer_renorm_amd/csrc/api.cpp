@@ -197,7 +197,8 @@ Layout layout(const moe_problem* p) {
     L.acc = 0;
     // fp32 rows, or fp16 rows (256-byte aligned) followed by their fp32 block factors
     const size_t f32_rows = (size_t)A * D * 4;
-    const size_t f16_rows = ((size_t)A * D * 2 + 255) / 256 * 256 + (size_t)A * ((D + 255) / 256) * 4;
+    const size_t f16_rows = ((size_t)A * D * 2 + 255) / 256 * 256 +
+                            (size_t)A * ((D + moe::kScaleCols - 1) / moe::kScaleCols) * 4;
     L.y_perm = take(f32_rows > f16_rows ? f32_rows : f16_rows);
     L.y_shared = take(has_shared(p) ? (size_t)T * D * 4 : 0);
   }
@@ -329,7 +330,7 @@ hipError_t run_down(const moe_problem* p, const void* H, const void* w_d, const 
     g.C = y_perm;
     g.ldc = p->D;
     g.c_scale = y_scale;  // fp16 rows with block factors (see compact_rows)
-    g.ldcs = (p->D + 255) / 256;
+    g.ldcs = (p->D + moe::kScaleCols - 1) / moe::kScaleCols;
     return launch_grouped(p, plan, moe::EPI_STORE, g, tiles, tile_count, max_mtiles, s);
   }
   g.acc_out = acc;
@@ -730,8 +731,9 @@ int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_
                   "shared expert launch");
     MOE_HIP_TRY(mark(MOE_STAGE_DOWN), "event record");
     if (compact_rows(p, plan)) {
-      // fp16 rows [A, D], then the fp32 block factors [A, ceil(D / 256)] (256-byte aligned)
-      const int nblk = (p->D + 255) / 256;
+      // fp16 rows [A, D], then the fp32 block factors [A, ceil(D / kScaleCols)] (256-byte
+      // aligned)
+      const int nblk = (p->D + moe::kScaleCols - 1) / moe::kScaleCols;
       float* y_scale = reinterpret_cast<float*>(
           reinterpret_cast<char*>(y_perm) + ((A * p->D * 2 + 255) / 256) * 256);
       MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, plan, y_perm,

@@ -69,7 +69,7 @@ __device__ __forceinline__ void store8(__bf16* dst, const float* a) {
   *(bf16x8*)dst = o;
 }
 
-// Gather-sum over fp16 expert rows with per-(row, 256-column block) factors: 8 columns per
+// Gather-sum over fp16 expert rows with per-(row, kScaleCols-column block) factors: 8 columns per
 // thread (one 16-byte load per slot), in slot order, then the shared branch, one rounding.
 template <typename OUT>
 __global__ void __launch_bounds__(256) combine16_kernel(const _Float16* __restrict__ y16,
@@ -89,7 +89,7 @@ __global__ void __launch_bounds__(256) combine16_kernel(const _Float16* __restri
       for (int k = 0; k < K; ++k) {
         const int pos = inv_perm[t * K + k];
         if (pos < 0) continue;  // sentinel or dropped assignment
-        const float w = topk_w[t * K + k] * ysc[(int64_t)pos * nblk + (d >> 8)];
+        const float w = topk_w[t * K + k] * ysc[(int64_t)pos * nblk + d / kScaleCols];
         const f16x8 v = *(const f16x8*)(y16 + (int64_t)pos * D + d);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += w * (float)v[i];

@@ -12,7 +12,8 @@
 //  * K advances 64 per stage (128 bytes of every row, so each row's line is requested once).
 //    Both operands move from L2/HBM straight into LDS with global_load_lds_dwordx4 (no staging
 //    registers), token rows in a 2-stage ring and weights, which stream from HBM, in a
-//    3-stage ring (32 KiB per operand stage, 160 KiB of LDS).
+//    3-stage ring (32 KiB per operand stage, 160 KiB of LDS; decode batches, whose tiles have
+//    at most 64 rows, use 8 KiB token-row stages).
 //  * The fragments of each 32-wide K step are read from LDS while the MFMAs of the previous
 //    one run (A fragments in place as their rows finish, B fragments into a second set), so
 //    LDS latency is hidden inside the wave; one barrier per stage publishes the next stage
@@ -21,11 +22,16 @@
 //    (r >> 1) & 7, which keeps the 16-row operand fetches conflict-free.
 //  * Token rows are gathered through the dispatch permutation by the DMA addresses themselves.
 //  * Persistent, XCD-aware schedule over logical tiles ordered expert-major, then N tile, then
-//    M tile, so the tiles that share an expert's weights or rows meet in one XCD's L2.
-//  * Epilogues are assembled in LDS (reusing the ring) and leave as whole chunks: fused
-//    SiLU·up (a wave's 8 column tiles are 4 gate/up pairs), fp32 store with an optional row
-//    scale, fp16 store with one power-of-two factor per tile, or the weighted fp32 atomic
-//    combine.
+//    M tile, so the tiles that share an expert's weights or rows meet in one XCD's L2.  With
+//    three or more K stages the rings run on across a work-group's tiles: a tile's last
+//    refills fetch the next tile's first stages.
+//  * Epilogues store straight from the accumulators, which hold the transposed tile (weights
+//    are the MFMA's first operand), so each lane writes 4 consecutive columns of a row: fused
+//    SiLU·up (a wave's 8 column tiles are 4 gate/up pairs), fp32 with an optional row scale,
+//    fp16 with a power-of-two factor per row and 128-column block, or the weighted fp32
+//    atomic combine.  No LDS is involved, so the next tile's loads fly meanwhile.
+#include <type_traits>
+
 #include "kernels.h"
 #include "silu.h"
 
@@ -40,8 +46,7 @@ constexpr int kBM = 256;       // tile rows (tokens)
 constexpr int kBN = 256;       // tile weight rows (output columns; half of them for SwiGLU)
 constexpr int kRow = 128;      // LDS bytes per staged row per stage (64 bf16: two MFMA K steps)
 constexpr int kSA = 2, kSB = 3;             // ring depths: token rows (L2-resident), weights
-constexpr int kAStage = kBM * kRow, kBStage = kBN * kRow;  // 32 KiB each
-constexpr int kLds = kSA * kAStage + kSB * kBStage;       // 160 KiB
+constexpr int kBStage = kBN * kRow;        // 32 KiB weight stage (token-row stages: 32 or 8 KiB)
 
 // s_waitcnt immediate (gfx9 layout): at most `vm` vector-memory and `lgkm` LDS/scalar
 // operations of this wave outstanding.
@@ -101,7 +106,10 @@ __device__ __forceinline__ void read_frags(const char* la, const char* lb, bf16x
 
 // The 8·MI MFMAs of one 32-wide K step, reading the next step's fragments in between: one of
 // the 8 next B fragments (into the other B set) after every MI MFMAs, A fragment i in place
-// right after row i's 8 MFMAs.
+// right after row i's 8 MFMAs.  The weight fragment goes in as the MFMA's first operand, so
+// each 16 x 16 accumulator holds the transposed output tile: lane (lr, lk) gets token row lr,
+// output columns 4 lk + [0, 4) (both operands have the same fragment layout, so the swap is
+// free and lets the epilogue store 4 consecutive columns per lane).
 template <int MI, bool SWIGLU>
 __device__ __forceinline__ void mma_stage(f32x4 (*acc)[8], bf16x8* af, const bf16x8* bfr,
                                           const char* la_n, const char* lb_n, bf16x8* bfr_n) {
@@ -109,7 +117,7 @@ __device__ __forceinline__ void mma_stage(f32x4 (*acc)[8], bf16x8* af, const bf1
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
       if ((i * 8 + j + 1) % MI == 0) {
         const int b = (i * 8 + j + 1) / MI - 1;
         bfr_n[b] = *(const bf16x8*)(lb_n + boff<SWIGLU>(b));
@@ -129,23 +137,301 @@ __device__ __forceinline__ int block_row0(int wm, int mi_hi, int mi_lo) {
   return wm < 2 ? wm * 16 * mi_hi : 32 * mi_hi + (wm - 2) * 16 * mi_lo;
 }
 
+// 32-row pairs of MFMA row tiles that hold `rows` rows, split over the wave row blocks: blocks
+// 0 and 1 take mi_hi 16-row tiles each, blocks 2 and 3 mi_lo.
+__device__ __forceinline__ void tile_mi(int rows, int* mi_hi, int* mi_lo) {
+  const int pairs = min(max((rows + 31) >> 5, 1), 8);
+  *mi_hi = (pairs + 1) >> 1;
+  *mi_lo = pairs >> 1;
+}
+
+// A tile of a work-group's schedule: its group (expert), rows [row_start, + rows) and N tile.
+struct TileMap {
+  int group, row_start, rows, n_tile;
+};
+
+// Logical tile t: expert-major, then N tile, then M tile (the M tiles of one expert are
+// entries [first, first + cnt) of the tile map and own logical tiles [first·ntN, (first+cnt)·ntN));
+// dense mode (no tile map) has one group of mt_total M tiles.  Decoding takes two dependent
+// rounds of scalar loads: the expert's entry (map_expert), then the M tile's (map_mtile).
+__device__ __forceinline__ void map_expert(const GemmParams& p, int t, int ntN, int mt_total,
+                                           int* first, int* cnt) {
+  if (p.tiles) {
+    const int q = t / ntN;
+    *first = load_uniform(p.tiles, q * kTileStride + 4);
+    *cnt = load_uniform(p.tiles, q * kTileStride + 5);
+  } else {
+    *first = 0;
+    *cnt = mt_total;
+  }
+}
+
+__device__ __forceinline__ void map_mtile(const GemmParams& p, int t, int ntN, int first, int cnt,
+                                          TileMap& tile) {
+  const int l = t - first * ntN;
+  tile.n_tile = l / cnt;
+  const int m = first + l % cnt;
+  if (p.tiles) {
+    tile.group = load_uniform(p.tiles, m * kTileStride + 0);
+    tile.row_start = load_uniform(p.tiles, m * kTileStride + 1);
+    tile.rows = load_uniform(p.tiles, m * kTileStride + 2);
+  } else {
+    tile.group = 0;
+    tile.row_start = m * kBM;
+    tile.rows = min(kBM, p.M - m * kBM);
+  }
+}
+
+// Staged row r = 8 (wave + 8 i) + (lane >> 3) of DMA instruction i keeps logical chunk
+// (lane & 7) ^ swz(r) in the lane's slot; swz depends on r mod 16 only, so one value serves
+// every instruction of the wave.
+__device__ __forceinline__ int lane_chunk(int lane, int wave) {
+  return (lane & 7) ^ swz(8 * wave + (lane >> 3));
+}
+
+template <bool SWIGLU>
+__device__ __forceinline__ void weight_sources(const GemmParams& p, int lane, int wave,
+                                               int n_tile, uint32_t* sb) {
+  const int chunk = lane_chunk(lane, wave);
+#pragma unroll
+  for (int i = 0; i < kDma; ++i) {
+    const int r = 8 * (wave + kNW * i) + (lane >> 3);
+    int brow;
+    if (SWIGLU) {
+      // the tile's first 128 staged rows are gate rows, the next 128 the matching up rows
+      const int n = n_tile * (kBN / 2) + (r & (kBN / 2 - 1));
+      brow = n < p.N ? (r < kBN / 2 ? n : p.N + n) : 0;
+    } else {
+      const int n = n_tile * kBN + r;
+      brow = n < p.N ? n : 0;
+    }
+    sb[i] = (uint32_t)brow * (uint32_t)p.ldb_bytes + chunk * 16;
+  }
+}
+
+// Token row of instruction i without a gather: position row_start + min(r, rows - 1).
+__device__ __forceinline__ uint32_t row_source(const GemmParams& p, int lane, int wave,
+                                               int row_start, int rows, int i) {
+  const int r = 8 * (wave + kNW * i) + (lane >> 3);
+  return (uint32_t)(row_start + min(r, rows - 1)) * (uint32_t)p.lda_bytes +
+         lane_chunk(lane, wave) * 16;
+}
+
+// Gathered token rows in two steps, so that all loads of a tile go out together.  gather_issue
+// reads the permutation entries of instruction i's 8 positions row_start + min(r0 + k,
+// rows - 1) with scalar loads (uniform addresses: no vector load is left for the compiler to
+// wait on, and a wait on the vector-memory counter would also wait for every DMA and store in
+// flight); gather_source picks the lane's.
+__device__ __forceinline__ void gather_issue(const GemmParams& p, int wave, int row_start,
+                                             int rows, int i, int* v) {
+  const int r0 = 8 * (wave + kNW * i);
+  if (r0 + 8 <= rows) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = load_uniform(p.a_gather, row_start + r0 + k);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = load_uniform(p.a_gather, row_start + min(r0 + k, rows - 1));
+  }
+}
+
+__device__ __forceinline__ uint32_t gather_source(const GemmParams& p, int lane, int wave,
+                                                  const int* v) {
+  // a tree of selects on the bits of q over values the compiler cannot trace back to the
+  // loads (selects between loaded values become an indexed private array, i.e. scratch)
+  int w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    w[k] = v[k];
+    asm volatile("" : "+s"(w[k]));
+  }
+  const int q = lane >> 3;
+  const bool b0 = q & 1, b1 = q & 2, b2 = q & 4;
+  const int a01 = b0 ? w[1] : w[0], a23 = b0 ? w[3] : w[2];
+  const int a45 = b0 ? w[5] : w[4], a67 = b0 ? w[7] : w[6];
+  const int a03 = b1 ? a23 : a01, a47 = b1 ? a67 : a45;
+  const int a = b2 ? a47 : a03;
+  return (uint32_t)(a / p.a_div) * (uint32_t)p.lda_bytes + lane_chunk(lane, wave) * 16;
+}
+
+__device__ __forceinline__ void load_map(const GemmParams& p, int t, int ntN, int mt_total,
+                                         TileMap& tile) {
+  int first, cnt;
+  map_expert(p, t, ntN, mt_total, &first, &cnt);
+  map_mtile(p, t, ntN, first, cnt, tile);
+}
+
+// Every DMA source of a tile: weight rows, and token rows of the first NA instructions (the
+// gathered ones in one round of loads).
+template <bool SWIGLU, int NA>
+__device__ __forceinline__ void tile_sources(const GemmParams& p, int lane, int wave,
+                                             const TileMap& tile, uint32_t* sa, uint32_t* sb) {
+  weight_sources<SWIGLU>(p, lane, wave, tile.n_tile, sb);
+  if (p.a_gather) {
+    int v[NA][8];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) gather_issue(p, wave, tile.row_start, tile.rows, i, v[i]);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) sa[i] = gather_source(p, lane, wave, v[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) sa[i] = row_source(p, lane, wave, tile.row_start, tile.rows, i);
+  }
+}
+
+// Token-row DMA of one stage with a run-time count n <= MAXN of instructions per wave.
+template <int MAXN>
+__device__ __forceinline__ void dma_rows_n(int n, const char* base, const uint32_t* src,
+                                           uint32_t off, char* stage, int wave) {
+#pragma unroll
+  for (int i = 0; i < MAXN; ++i)
+    if (i < n)
+      __builtin_amdgcn_global_load_lds(base + (src[i] + off), stage + (wave + kNW * i) * 1024, 16,
+                                       0, 0);
+}
+
+// Epilogue straight from the accumulators.  The weight fragment is the MFMA's first operand,
+// so lane (lr, lk) of MFMA tile (i, j) holds row wrow0 + 16 i + lr of the output tile and
+// columns 16 j + 4 lk + [0, 4) of its wave's column block: every lane writes 4 consecutive
+// columns of one row, and an MFMA tile leaves as 16 row runs of 32 (bf16, fp16) or 64 (fp32)
+// bytes that L2 merges with the neighbouring tiles' into whole lines.  No LDS, no barrier.
+template <int MI, int EPI, bool RS>
+__device__ __forceinline__ void store_tile(const GemmParams& p, const f32x4 (*acc)[8], int lane,
+                                           int wn, int wrow0, int row_start, int rows,
+                                           int n_tile) {
+  const int lr = lane & 15, c4 = (lane >> 4) * 4;
+  if constexpr (EPI == EPI_SWIGLU) {
+    // H: the tile's 128 columns; wave wn holds [64 wn, +64) as gate tiles j and up tiles j + 4
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const int ncols = min(kBN / 2, p.N - n_tile * (kBN / 2));
+    __bf16* Ht = (__bf16*)p.C + (int64_t)row_start * p.ldc + n_tile * (kBN / 2);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int row = wrow0 + 16 * i + lr;
+      if (row < rows) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = wn * 64 + 16 * j + c4;
+          if (col < ncols) {
+            bf16x4 h;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              h[r] = (__bf16)(silu_fast(acc[i][j][r]) * acc[i][j + 4][r]);
+            *(bf16x4*)(Ht + (int64_t)row * p.ldc + col) = h;
+          }
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_STORE) {
+    static_assert(kScaleCols == kBN / 2, "one fp16 factor block per wave column half");
+    const int ncols = min(kBN, p.N - n_tile * kBN);
+    const int c0 = wn * 128;  // this wave's columns [c0, c0 + 128) of the tile
+    if (p.c_scale) {
+      // fp16 with a power-of-two factor per row of the wave's 128 columns, from the row's
+      // largest |value| (the lane's 32 values, then the 4 lanes that share the row)
+      _Float16* Ch = (_Float16*)p.C + (int64_t)row_start * p.ldc + n_tile * kBN;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (c0 + 16 * j < ncols)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[i][j][r]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float sc, inv;
+        f16_block_scale(mx, &sc, &inv);
+        const int row = wrow0 + 16 * i + lr;
+        if (row < rows && c0 < ncols) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int col = c0 + 16 * j + c4;
+            if (col < ncols) {
+              const f16x4 h = {(_Float16)(acc[i][j][0] * sc), (_Float16)(acc[i][j][1] * sc),
+                               (_Float16)(acc[i][j][2] * sc), (_Float16)(acc[i][j][3] * sc)};
+              *(f16x4*)(Ch + (int64_t)row * p.ldc + col) = h;
+            }
+          }
+          if (lane < 16)
+            p.c_scale[(int64_t)(row_start + row) * p.ldcs + n_tile * (kBN / kScaleCols) + wn] =
+                inv;
+        }
+      }
+    } else {
+      // fp32, times row_scale[row] in the RS variant (its vector load is waited for at once,
+      // which also waits for the next tile's first stages; the variant serves only the
+      // row-scaled shared expert)
+      float* Ct = (float*)p.C + (int64_t)row_start * p.ldc + n_tile * kBN;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int row = wrow0 + 16 * i + lr;
+        if (row < rows) {
+          float s = 1.0f;
+          if constexpr (RS) s = p.row_scale[row_start + row];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int col = c0 + 16 * j + c4;
+            if (col < ncols) {
+              f32x4 v = acc[i][j];
+              if constexpr (RS) v *= s;
+              *(f32x4*)(Ct + (int64_t)row * p.ldc + col) = v;
+            }
+          }
+        }
+      }
+    }
+  } else {  // EPI_ATOMIC_COMBINE: the token's output row += routing weight * row
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int row = wrow0 + 16 * i + lr;
+      if (row < rows) {
+        const int a = p.perm[row_start + row];
+        const float w = p.topk_w[a];
+        const int n0 = n_tile * kBN + wn * 128;
+        float* dst = p.acc_out + (int64_t)(a / p.topk) * p.ldo + n0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int n = 16 * j + c4 + r;
+            if (n0 + n < p.N) unsafeAtomicAdd(dst + n, w * acc[i][j][r]);
+          }
+      }
+    }
+  }
+}
+
 // One output tile.  Wave (wm, wn) owns MI x 8 MFMA tiles of 16 x 16: columns [128 wn, +128)
 // and MI 16-row tiles starting at block_row0(wm).  A tile of `rows` rows is computed as
-// P = ceil(rows / 32) pairs of 16-row tiles: row blocks 0 and 1 take mi_hi = ceil(P / 2) each,
-// blocks 2 and 3 mi_lo = floor(P / 2).  The two waves that share a SIMD (waves w and w + 4)
-// hold one block of each kind, so every SIMD runs P sets of 8 MFMAs per K step and a partly
-// filled tile (a group's last one) costs in proportion to its rows, to 32 rows.  Only the
-// token rows [0, 32 P) are fetched; MI is also this wave's count of 1 KiB token-row DMA
-// instructions per stage.
-template <int MI, int EPI>
-__device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int tid, int wave,
-                                          int group, int row_start, int rows, int n_tile,
-                                          int ns, int mi_hi, int mi_lo) {
+// P = ceil(rows / 32) pairs of 16-row tiles (tile_mi): row blocks 0 and 1 take mi_hi =
+// ceil(P / 2) each, blocks 2 and 3 mi_lo = floor(P / 2).  The two waves that share a SIMD
+// (waves w and w + 4) hold one block of each kind, so every SIMD runs P sets of 8 MFMAs per K
+// step and a partly filled tile (a group's last one) costs in proportion to its rows, to 32
+// rows.  Only the token rows [0, 32 P) are fetched; MI is also this wave's count of 1 KiB
+// token-row DMA instructions per stage.
+//
+// Rings: token rows in 2 stages of AROWS x 128 bytes, weights in 3 stages of 32 KiB.  Global
+// stage G (the work-group's running count, this tile's stage 0 is G0) lives in slots G % 2 and
+// G % 3.  When the reduction has at least 3 stages the rings run on across the work-group's
+// tiles: the refills during a tile's last three stages fetch the next tile's stages 0-2 (nx_*
+// describe it, nx_group < 0 if there is none, and nx_mi is this wave's MI there), and that
+// tile then starts with them in flight or landed (`pre`), so the weight stream does not stop
+// for an epilogue or a prologue.
+template <int MI, int EPI, int AROWS, bool RS>
+__device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int tid, int wave,
+                                          const TileMap& cur, int ns, int mi_hi, int mi_lo,
+                                          int G0, bool pre, int tn, int ntN, int mt_total,
+                                          TileMap& nx) {
   constexpr bool kSwiglu = EPI == EPI_SWIGLU;
+  constexpr int kAS = AROWS * kRow;  // token-row stage bytes
+  constexpr int kMaxMI = AROWS / 64;
   constexpr int MIA = MI > 0 ? MI : 1;  // array extent
-  static_assert(MI >= 0 && MI <= 4 && kDma == 4 && 4 * kDma < 64, "tile shape, vmcnt range");
-  char* const sA = smem;                  // token-row ring, kSA stages
-  char* const sB = smem + kSA * kAStage;  // weight ring, kSB stages
+  static_assert(MI >= 0 && MI <= kMaxMI && kSA == 2 && kSB == 3, "tile shape, ring depths");
+  static_assert(kDma == 4 && 2 * kDma + kMaxMI < 64, "vmcnt range");
+  char* const sA = smem;             // token-row ring
+  char* const sB = smem + kSA * kAS;  // weight ring
+  const auto a_at = [&](int G) { return sA + (G & 1) * kAS; };
+  const auto b_at = [&](int G) { return sB + (G % 3) * kBStage; };
   const int lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 15, lk = lane >> 4;
@@ -158,25 +444,21 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
   const int lb_row = ((kSwiglu ? wn * 64 : wn * 128) + lr) * kRow;
   const int ch0 = (lk ^ swz(lr)) << 4, ch1 = ((4 + lk) ^ swz(lr)) << 4;
 
-  // ---- global source of each DMA chunk this lane issues per stage ----------------------------
-  const char* gbase = p.B + (int64_t)group * p.b_group_bytes;
-  uint32_t srcA[kDma], srcB[kDma];
-#pragma unroll
-  for (int i = 0; i < kDma; ++i) {
-    const int r = 8 * (wave + kNW * i) + (lane >> 3);  // staged row of either operand
-    const int chunk = (lane & 7) ^ swz(r);            // logical chunk kept in this slot
-    const int pos = row_start + min(r, rows - 1);
-    const int arow = p.a_gather ? p.a_gather[pos] / p.a_div : pos;
-    srcA[i] = (uint32_t)arow * (uint32_t)p.lda_bytes + chunk * 16;
-    int brow;
-    if (kSwiglu) {
-      const int n = n_tile * (kBN / 2) + (r & (kBN / 2 - 1));
-      brow = n < p.N ? (r < kBN / 2 ? n : p.N + n) : 0;
-    } else {
-      const int n = n_tile * kBN + r;
-      brow = n < p.N ? n : 0;
-    }
-    srcB[i] = (uint32_t)brow * (uint32_t)p.ldb_bytes + chunk * 16;
+  const int rows = cur.rows;
+  uint32_t srcA[kMaxMI], srcB[kDma], nsA[kMaxMI], nsB[kDma];
+  tile_sources<kSwiglu, kMaxMI>(p, lane, wave, cur, srcA, srcB);
+  const char* gbase = p.B + (int64_t)cur.group * p.b_group_bytes;
+
+  // The next tile (logical tile tn >= 0), whose first stages this tile's last refills fetch:
+  // its map entry (returned in nx for the caller) and DMA sources.
+  const bool nxt = tn >= 0;
+  int nx_mi = 0;  // this wave's token-row DMA instructions per stage of the next tile
+  if (nxt) {
+    load_map(p, tn, ntN, mt_total, nx);
+    tile_sources<kSwiglu, kMaxMI>(p, lane, wave, nx, nsA, nsB);
+    int nh, nl;
+    tile_mi(nx.rows, &nh, &nl);
+    nx_mi = wave < 4 ? nh : nl;
   }
 
   f32x4 acc[MIA][8];
@@ -185,343 +467,15 @@ __device__ __forceinline__ void mfma_tile(const GemmParams& p, char* smem, int t
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // every wave is done with the previous tile's LDS (epilogue staging) before new DMA lands
-  barrier_after<0, 0>();
-  // Ring schedule (per wave, in issue order): prologue A0 B0 A1 B1 B2, then before stage g+1
-  // is used, A(g+2) B(g+3).  Token rows run two stages ahead, weights three, so up to 64 KiB
-  // of weights per CU are in flight.  A stage of token rows is MI instructions per wave, one
-  // of weights kDma; the waits below count exactly those.
-  dma_operand<kNW, MI>(p.A, srcA, 0, sA, wave);
-  dma_operand<kNW>(gbase, srcB, 0, sB, wave);
-  if (ns > 1) {
-    dma_operand<kNW, MI>(p.A, srcA, kRow, sA + kAStage, wave);
-    dma_operand<kNW>(gbase, srcB, kRow, sB + kBStage, wave);
-  }
-  if (ns > 2) dma_operand<kNW>(gbase, srcB, 2 * kRow, sB + 2 * kBStage, wave);
-
-  // stage 0 published, its first half's fragments read (A fragments are refilled in place,
-  // B fragments alternate between two sets)
-  bf16x8 af0[MIA], bf0[8], bf1[8];
-  if (ns > 2)  // A1 B1 B2 were issued after B0 and may still fly
-    barrier_after<MI + 2 * kDma, 0>();
-  else
-    barrier_after<0, 0>();
-  if constexpr (MI > 0) read_frags<MI, kSwiglu>(sA + la_row + ch0, sB + lb_row + ch0, af0, bf0);
-
-  // Stage g's MFMAs: first half (step 2g) while reading the second half's fragments from
-  // the same stage; then publish stage g+1 (this wave's copies landed; every wave has read
-  // all of stage g, so its buffers are free), refill them with A(g+2) and B(g+3), and run the
-  // second half (step 2g+1) while reading stage g+1's first half.
-  for (int g = 0; g < ns; ++g) {
-    const char* ca = sA + (g % kSA) * kAStage;
-    const char* cb = sB + (g % kSB) * kBStage;
-    if constexpr (MI > 0)
-      mma_stage<MI, kSwiglu>(acc, af0, bf0, ca + la_row + ch1, cb + lb_row + ch1, bf1);
-    if (g + 1 < ns) {
-      if (g + 2 < ns)  // B(g+2) went out after A(g+1) and may still fly
-        barrier_after<kDma, 0>();
-      else
-        barrier_after<0, 0>();
-      if (g + 2 < ns)
-        dma_operand<kNW, MI>(p.A, srcA, (uint32_t)(g + 2) * kRow, sA + (g % kSA) * kAStage,
-                             wave);
-      if (g + 3 < ns)
-        dma_operand<kNW>(gbase, srcB, (uint32_t)(g + 3) * kRow, sB + (g % kSB) * kBStage, wave);
-    }
-    // after the last stage these reads fetch unused leftovers
-    const char* na = sA + ((g + 1) % kSA) * kAStage;
-    const char* nb = sB + ((g + 1) % kSB) * kBStage;
-    if constexpr (MI > 0)
-      mma_stage<MI, kSwiglu>(acc, af0, bf1, na + la_row + ch0, nb + lb_row + ch0, bf0);
-  }
-
-  // ---- epilogue (staged in the ring's LDS) ---------------------------------------------------
-  // Lane (lr, lk) holds rows wrow0 + 16 i + 4 lk + r of column tile j in acc[i][j][r].  The
-  // thread index is laundered through an empty asm so the store offsets below are computed
-  // here, not hoisted out of the tile loop into registers (and spilled).
-  int etid = tid;
-  asm volatile("" : "+v"(etid));
-  const int elr = etid & 15, elk = (etid >> 4) & 3;
-  barrier_after<0, 0>();  // all waves are done reading the ring
-  if constexpr (kSwiglu) {
-    // H tile: up to 256 rows x 128 columns of the layer dtype, 272-byte LDS rows
-    constexpr int kLdH = kBN / 2 + 8;
-    __bf16* Eh = (__bf16*)smem;
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = wrow0 + i * 16 + elk * 4 + r;
-          const int col = wn * 64 + j * 16 + elr;
-          Eh[row * kLdH + col] = (__bf16)(silu_fast(acc[i][j][r]) * acc[i][j + 4][r]);
-        }
-    barrier_after<0, 0>();
-    constexpr int kCpr = kBN / 2 / 8;  // 16 chunks of 8 values per H row
-    char* Ht = (char*)p.C + ((int64_t)row_start * p.ldc + n_tile * (kBN / 2)) * 2;
-    const int ncols = min(kBN / 2, p.N - n_tile * (kBN / 2));
-    const int nmm = (rows * kCpr + kNT - 1) / kNT;
-    for (int mm = 0; mm < nmm; ++mm) {
-      const int c = etid + kNT * mm;
-      const int row = c / kCpr, ch = c % kCpr;
-      if (row < rows && ch * 8 < ncols)
-        *(bf16x8*)(Ht + (uint32_t)(row * (int)p.ldc + ch * 8) * 2u) =
-            *(const bf16x8*)(Eh + row * kLdH + ch * 8);
-    }
-  } else if constexpr (EPI == EPI_STORE) {
-    // fp32 tile in four passes, one per wave row block (up to 64 rows x 256 columns, 1040-byte
-    // LDS rows), each written to LDS by the two waves that own it
-    constexpr int kLdE = kBN + 4;
-    float* E = (float*)smem;
-    // fp16 rows: one power-of-two factor for the tile, from its largest |value| (reduced over
-    // the lane, the wave, then the 8 waves through LDS past the staging area)
-    float sc = 1.0f, inv = 1.0f;
-    if (p.c_scale) {
-      float* tmax = (float*)(smem + kLds - 64);
-      float mx = 0.0f;
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[i][j][r]));
-      mx = wave_max_abs(mx);
-      if ((etid & 63) == 0) tmax[wave] = mx;
-      barrier_after<0, 0>();
-      mx = tmax[0];
-#pragma unroll
-      for (int w = 1; w < kNW; ++w) mx = fmaxf(mx, tmax[w]);
-      f16_block_scale(mx, &sc, &inv);
-    }
-    char* Ct = (char*)p.C + ((int64_t)row_start * p.ldc + n_tile * kBN) * 4;
-    char* Ch = (char*)p.C + ((int64_t)row_start * p.ldc + n_tile * kBN) * 2;
-    const float* rs = p.row_scale ? p.row_scale + row_start : nullptr;
-    const int ncols = min(kBN, p.N - n_tile * kBN);
-    constexpr int kCpr = kBN / 4;  // 16-byte chunks per fp32 row
-#pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int prow0 = block_row0(pass, mi_hi, mi_lo);
-      const int pmi = pass < 2 ? mi_hi : mi_lo;
-      if (pmi > 0 && prow0 < rows) {  // uniform
-        if (wm == pass) {
-#pragma unroll
-          for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                E[(i * 16 + elk * 4 + r) * kLdE + wn * 128 + j * 16 + elr] = acc[i][j][r];
-        }
-        barrier_after<0, 0>();
-        for (int mm = 0; mm < 2 * pmi; ++mm) {  // 16 pmi rows of kCpr chunks
-          const int c = etid + kNT * mm;
-          const int lrow = c / kCpr, col = (c % kCpr) * 4;  // one row per wave
-          const int row = prow0 + lrow;
-          if (p.c_scale) {
-            // fp16 with the tile's power-of-two factor
-            const f32x4 v = *(const f32x4*)(E + lrow * kLdE + col);
-            if (row < rows) {
-              if (col < ncols) {
-                const f16x4 h = {(_Float16)(v[0] * sc), (_Float16)(v[1] * sc),
-                                 (_Float16)(v[2] * sc), (_Float16)(v[3] * sc)};
-                *(f16x4*)(Ch + (uint32_t)(row * (int)p.ldc + col) * 2u) = h;
-              }
-              if ((etid & 63) == 0) p.c_scale[(int64_t)(row_start + row) * p.ldcs + n_tile] = inv;
-            }
-          } else if (row < rows && col < ncols) {
-            f32x4 v = *(const f32x4*)(E + lrow * kLdE + col);
-            if (rs) v *= rs[row];
-            *(f32x4*)(Ct + (uint32_t)(row * (int)p.ldc + col) * 4u) = v;
-          }
-        }
-        barrier_after<0, 0>();
-      }
-    }
-  } else {  // EPI_ATOMIC_COMBINE
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wrow0 + i * 16 + elk * 4 + r;
-        if (row >= rows) continue;
-        const int a = p.perm[row_start + row];
-        const float w = p.topk_w[a];
-        float* dst = p.acc_out + (int64_t)(a / p.topk) * p.ldo;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int n = n_tile * kBN + wn * 128 + j * 16 + elr;
-          if (n < p.N) unsafeAtomicAdd(dst + n, w * acc[i][j][r]);
-        }
-      }
-  }
-}
-
-// Logical tile t: expert-major, then N tile, then M tile (the m-tiles of one expert are
-// entries [first, first + cnt) of the tile map and own logical tiles [first·ntN, (first+cnt)·ntN));
-// dense mode (no tile map) has one group of mt_total M tiles.
-__device__ __forceinline__ void decode_mtile(const GemmParams& p, int t, int ntN, int mt_total,
-                                             int* group, int* row_start, int* rows,
-                                             int* n_tile) {
-  const int q = t / ntN;
-  int first = 0, cnt = mt_total;
-  if (p.tiles) {
-    first = load_uniform(p.tiles, q * kTileStride + 4);
-    cnt = load_uniform(p.tiles, q * kTileStride + 5);
-  }
-  const int l = t - first * ntN;
-  *n_tile = l / cnt;
-  const int m = first + l % cnt;
-  if (p.tiles) {
-    *group = load_uniform(p.tiles, m * kTileStride + 0);
-    *row_start = load_uniform(p.tiles, m * kTileStride + 1);
-    *rows = load_uniform(p.tiles, m * kTileStride + 2);
-  } else {
-    *group = 0;
-    *row_start = m * kBM;
-    *rows = min(kBM, p.M - m * kBM);
-  }
-}
-
-template <int EPI>
-__global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-mfma_kernel(const GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem[kLds];
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  constexpr int BNE = EPI == EPI_SWIGLU ? kBN / 2 : kBN;  // output columns per tile
-  const int ntN = (p.N + BNE - 1) / BNE;
-  const int mt_total = p.tiles ? load_uniform(p.tile_count, 0) : (p.M + kBM - 1) / kBM;
-  const int nt = mt_total * ntN;
-  const int xcd = blockIdx.x % kXcds, per = gridDim.x / kXcds, jb = blockIdx.x / kXcds;
-  const int lo = (int)((int64_t)nt * xcd / kXcds), hi = (int)((int64_t)nt * (xcd + 1) / kXcds);
-  const int ns = p.Kdim / 64;  // DMA stages (Kdim is a multiple of 64)
-
-  for (int t = lo + jb; t < hi; t += per) {
-    // ---- logical tile: expert-major, then N tile, then M tile -------------------------------
-    const int q = t / ntN;
-    int first = 0, cnt = mt_total;
-    if (p.tiles) {
-      first = load_uniform(p.tiles, q * kTileStride + 4);
-      cnt = load_uniform(p.tiles, q * kTileStride + 5);
-    }
-    const int l = t - first * ntN;
-    const int n_tile = l / cnt;
-    const int m = first + l % cnt;
-    int group = 0, row_start = m * kBM, rows = min(kBM, p.M - m * kBM);
-    if (p.tiles) {
-      group = load_uniform(p.tiles, m * kTileStride + 0);
-      row_start = load_uniform(p.tiles, m * kTileStride + 1);
-      rows = load_uniform(p.tiles, m * kTileStride + 2);
-    }
-    // 32-row pairs of MFMA row tiles that hold rows, split over the wave row blocks
-    const int pairs = min(max((rows + 31) >> 5, 1), 8);
-    const int mi_hi = (pairs + 1) >> 1, mi_lo = pairs >> 1;
-    switch (wave < 4 ? mi_hi : mi_lo) {  // waves 0-3 hold row blocks 0 and 1
-      case 0:
-        mfma_tile<0, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns, mi_hi, mi_lo);
-        break;
-      case 1:
-        mfma_tile<1, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns, mi_hi, mi_lo);
-        break;
-      case 2:
-        mfma_tile<2, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns, mi_hi, mi_lo);
-        break;
-      case 3:
-        mfma_tile<3, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns, mi_hi, mi_lo);
-        break;
-      default:
-        mfma_tile<4, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns, mi_hi, mi_lo);
-        break;
-    }
-  }
-}
-
-// ---- batches of at most 64 tokens (decode) -----------------------------------------------
-// Every tile then has at most 64 rows, so a token-row stage takes 8 KiB, and the LDS holds the
-// two rings (2 x 8 KiB of token rows, 3 x 32 KiB of weights) and a separate 48 KiB staging
-// area for the epilogue.  The rings run on across the tiles of a work-group: the refills of a
-// tile's last three stages fetch the next tile's first stages (global stage G = the work-group's
-// stage count, ring slots G % 2 and G % 3), so the next tile starts with its prologue in LDS
-// and the weight stream never stops for a tile's epilogue or its first loads.
-constexpr int kSmallRows = 64;
-constexpr int kSmallAStage = kSmallRows * kRow;             // 8 KiB
-constexpr int kSmallStg = 2 * kSmallAStage + 3 * kBStage;  // staging area: [112 KiB, 160 KiB)
-
-// The lane's DMA source offsets for one tile: token rows (gathered) and weight rows.
-template <bool SWIGLU>
-__device__ __forceinline__ void tile_sources(const GemmParams& p, int lane, int wave,
-                                             int row_start, int rows, int n_tile, uint32_t* sa,
-                                             uint32_t* sb) {
-#pragma unroll
-  for (int i = 0; i < kDma; ++i) {
-    const int r = 8 * (wave + kNW * i) + (lane >> 3);  // staged row of either operand
-    const int chunk = (lane & 7) ^ swz(r);            // logical chunk kept in this slot
-    const int pos = row_start + min(r, rows - 1);
-    const int arow = p.a_gather ? p.a_gather[pos] / p.a_div : pos;
-    sa[i] = (uint32_t)arow * (uint32_t)p.lda_bytes + chunk * 16;
-    int brow;
-    if (SWIGLU) {
-      const int n = n_tile * (kBN / 2) + (r & (kBN / 2 - 1));
-      brow = n < p.N ? (r < kBN / 2 ? n : p.N + n) : 0;
-    } else {
-      const int n = n_tile * kBN + r;
-      brow = n < p.N ? n : 0;
-    }
-    sb[i] = (uint32_t)brow * (uint32_t)p.ldb_bytes + chunk * 16;
-  }
-}
-
-// Token-row DMA of one stage with a run-time count of instructions (0 or 1 here).
-__device__ __forceinline__ void dma_rows_small(int n, const char* base, const uint32_t* src,
-                                               uint32_t off, char* stage, int wave) {
-  if (n > 0) dma_operand<kNW, 1>(base, src, off, stage, wave);
-}
-
-// One tile of a small batch.  MI (0 or 1) is this wave's count of 16-row MFMA tiles and of
-// token-row DMA instructions per stage; nx_* describe the work-group's next tile (nx_group < 0:
-// none), nx_mi this wave's MI there.  G0 is the global index of this tile's stage 0; `pre`:
-// its stages 0-2 were issued by the previous tile.
-template <int MI, int EPI>
-__device__ __forceinline__ void small_tile(const GemmParams& p, char* smem, int tid, int wave,
-                                           int group, int row_start, int rows, int n_tile,
-                                           int ns, int mi_hi, int mi_lo, int G0, bool pre,
-                                           int nx_group, int nx_row_start, int nx_rows,
-                                           int nx_n_tile, int nx_mi) {
-  constexpr bool kSwiglu = EPI == EPI_SWIGLU;
-  static_assert(MI == 0 || MI == 1, "at most 64 rows: one 16-row MFMA tile per wave");
-  char* const sA = smem;                      // token-row ring, 2 stages of 8 KiB
-  char* const sB = smem + 2 * kSmallAStage;   // weight ring, 3 stages
-  char* const stg = smem + kSmallStg;         // epilogue staging
-  const auto a_at = [&](int G) { return sA + (G & 1) * kSmallAStage; };
-  const auto b_at = [&](int G) { return sB + (G % 3) * kBStage; };
-  const int lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 15, lk = lane >> 4;
-  const int wrow0 = block_row0(wm, mi_hi, mi_lo);
-  const int la_row = (wrow0 + lr) * kRow;
-  const int lb_row = ((kSwiglu ? wn * 64 : wn * 128) + lr) * kRow;
-  const int ch0 = (lk ^ swz(lr)) << 4, ch1 = ((4 + lk) ^ swz(lr)) << 4;
-
-  uint32_t srcA[kDma], srcB[kDma], nsA[kDma], nsB[kDma];
-  tile_sources<kSwiglu>(p, lane, wave, row_start, rows, n_tile, srcA, srcB);
-  const char* gbase = p.B + (int64_t)group * p.b_group_bytes;
-  const bool nxt = nx_group >= 0;
-  const char* nbase = p.B + (int64_t)(nxt ? nx_group : 0) * p.b_group_bytes;
-  if (nxt) tile_sources<kSwiglu>(p, lane, wave, nx_row_start, nx_rows, nx_n_tile, nsA, nsB);
-
-  f32x4 acc[1][8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   if (!pre) {
-    // first tile of the work-group: prologue A0 B0 A1 B1 B2
-    barrier_after<0, 0>();
-    dma_rows_small(MI, p.A, srcA, 0, a_at(G0), wave);
+    // Prologue A0 B0 A1 B1 B2, once every wave is done reading the previous tile's ring.
+    // Token rows run two stages ahead, weights three, so up to 64 KiB of weights per CU are
+    // in flight; a stage of token rows is MI instructions per wave, one of weights kDma.
+    lds_barrier();
+    dma_operand<kNW, MI>(p.A, srcA, 0, a_at(G0), wave);
     dma_operand<kNW>(gbase, srcB, 0, b_at(G0), wave);
     if (ns > 1) {
-      dma_rows_small(MI, p.A, srcA, kRow, a_at(G0 + 1), wave);
+      dma_operand<kNW, MI>(p.A, srcA, kRow, a_at(G0 + 1), wave);
       dma_operand<kNW>(gbase, srcB, kRow, b_at(G0 + 1), wave);
     }
     if (ns > 2) dma_operand<kNW>(gbase, srcB, 2 * kRow, b_at(G0 + 2), wave);
@@ -530,23 +484,48 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, char* smem, int 
     else
       barrier_after<0, 0>();
   } else {
-    // stages 0-2 came with the previous tile's last refills: drain them and its stores
-    barrier_after<0, 0>();
+    // Stages 0-2 went out with the previous tile's last refills, as B0 A0 B1 A1 B2, followed by
+    // its stores.  Loads complete in order, so A0 and B0 have landed once at most the
+    // 2 kDma + MI loads issued after A0 are outstanding (the stores are counted too, which
+    // can only lengthen the wait).
+    barrier_after<2 * kDma + MI, 0>();
   }
 
-  bf16x8 af0[1], bf0[8], bf1[8];
+  // stage 0's first half's fragments (A fragments are refilled in place, B fragments alternate
+  // between two sets)
+  bf16x8 af0[MIA], bf0[8], bf1[8];
   if constexpr (MI > 0)
-    read_frags<1, kSwiglu>(a_at(G0) + la_row + ch0, b_at(G0) + lb_row + ch0, af0, bf0);
+    read_frags<MI, kSwiglu>(a_at(G0) + la_row + ch0, b_at(G0) + lb_row + ch0, af0, bf0);
 
-  for (int g = 0; g < ns; ++g) {
-    const int G = G0 + g;
+  // Stage g's MFMAs: first half (step 2g) while reading the second half's fragments from the
+  // same stage; then publish stage g+1 (this wave's copies landed; every wave has read all of
+  // stage g, so its slots are free), refill them with token rows of stage g+2 and weights of
+  // g+3 (this tile's or, in the last three stages, the next tile's), and run the second half
+  // (step 2g+1) while reading stage g+1's first half.  ra and rb are the ring slots of stage
+  // g (global stage G0 + g modulo 2 and 3).
+  int ra = G0 & 1, rb = G0 % 3;
+  int g = 0;
+  for (; g + 3 < ns; ++g) {  // refills of this tile only
+    const int ra1 = ra ^ 1, rb1 = rb == 2 ? 0 : rb + 1;
     if constexpr (MI > 0)
-      mma_stage<1, kSwiglu>(acc, af0, bf0, a_at(G) + la_row + ch1, b_at(G) + lb_row + ch1, bf1);
-    // Publish stage g+1: this wave's copies landed (B(G+2), refilled one stage ago after
-    // A(G+1), may still fly, unless nothing refilled it); every wave has read stage g, whose
-    // slots take global stages G+2 (token rows) and G+3 (weights) of this tile or the next.
+      mma_stage<MI, kSwiglu>(acc, af0, bf0, sA + ra * kAS + la_row + ch1,
+                             sB + rb * kBStage + lb_row + ch1, bf1);
+    barrier_after<kDma, 0>();  // B(g+2) went out after A(g+1) and may still fly
+    dma_operand<kNW, MI>(p.A, srcA, (uint32_t)(g + 2) * kRow, sA + ra * kAS, wave);
+    dma_operand<kNW>(gbase, srcB, (uint32_t)(g + 3) * kRow, sB + rb * kBStage, wave);
+    if constexpr (MI > 0)
+      mma_stage<MI, kSwiglu>(acc, af0, bf1, sA + ra1 * kAS + la_row + ch0,
+                             sB + rb1 * kBStage + lb_row + ch0, bf0);
+    ra = ra1;
+    rb = rb1;
+  }
+  for (; g < ns; ++g) {  // the last three stages
+    const int ra1 = ra ^ 1, rb1 = rb == 2 ? 0 : rb + 1;
+    if constexpr (MI > 0)
+      mma_stage<MI, kSwiglu>(acc, af0, bf0, sA + ra * kAS + la_row + ch1,
+                             sB + rb * kBStage + lb_row + ch1, bf1);
     if (g + 1 < ns) {
-      if (g + 2 < ns || nxt || g == 0)
+      if (g + 2 < ns || nxt)  // B(g+2) went out after A(g+1) and may still fly
         barrier_after<kDma, 0>();
       else
         barrier_after<0, 0>();
@@ -554,172 +533,89 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, char* smem, int 
       lds_barrier();  // the last stage: nothing to wait for, the slots are free
     }
     if (g + 2 < ns)
-      dma_rows_small(MI, p.A, srcA, (uint32_t)(g + 2) * kRow, a_at(G + 2), wave);
+      dma_operand<kNW, MI>(p.A, srcA, (uint32_t)(g + 2) * kRow, sA + ra * kAS, wave);
     else if (nxt)
-      dma_rows_small(nx_mi, p.A, nsA, (uint32_t)(g + 2 - ns) * kRow, a_at(G + 2), wave);
-    if (g + 3 < ns)
-      dma_operand<kNW>(gbase, srcB, (uint32_t)(g + 3) * kRow, b_at(G + 3), wave);
-    else if (nxt)
-      dma_operand<kNW>(nbase, nsB, (uint32_t)(g + 3 - ns) * kRow, b_at(G + 3), wave);
+      dma_rows_n<kMaxMI>(nx_mi, p.A, nsA, (uint32_t)(g + 2 - ns) * kRow, sA + ra * kAS, wave);
+    if (nxt)  // g + 3 >= ns here: the next tile's weights
+      dma_operand<kNW>(p.B + (int64_t)nx.group * p.b_group_bytes, nsB,
+                       (uint32_t)(g + 3 - ns) * kRow, sB + rb * kBStage, wave);
     if constexpr (MI > 0) {
-      if (g + 1 < ns)
-        mma_stage<1, kSwiglu>(acc, af0, bf1, a_at(G + 1) + la_row + ch0, b_at(G + 1) + lb_row + ch0,
-                              bf0);
-      else
-        mma_stage<1, kSwiglu>(acc, af0, bf1, a_at(G) + la_row + ch0, b_at(G) + lb_row + ch0, bf0);
+      // after the last stage these reads fetch unused leftovers
+      const int na = g + 1 < ns ? ra1 : ra, nb = g + 1 < ns ? rb1 : rb;
+      mma_stage<MI, kSwiglu>(acc, af0, bf1, sA + na * kAS + la_row + ch0,
+                             sB + nb * kBStage + lb_row + ch0, bf0);
     }
+    ra = ra1;
+    rb = rb1;
   }
 
-  // ---- epilogue, staged in its own LDS area (only LDS barriers: the next tile's loads fly) --
-  int etid = tid;
-  asm volatile("" : "+v"(etid));
-  const int elr = etid & 15, elk = (etid >> 4) & 3;
-  if constexpr (kSwiglu) {
-    constexpr int kLdH = kBN / 2 + 8;  // up to 64 rows x 128 columns, 272-byte rows
-    __bf16* Eh = (__bf16*)stg;
-    if constexpr (MI > 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = wrow0 + elk * 4 + r;
-          const int col = wn * 64 + j * 16 + elr;
-          Eh[row * kLdH + col] = (__bf16)(silu_fast(acc[0][j][r]) * acc[0][j + 4][r]);
-        }
-    }
-    lds_barrier();
-    constexpr int kCpr = kBN / 2 / 8;  // 16 chunks of 8 values per H row
-    char* Ht = (char*)p.C + ((int64_t)row_start * p.ldc + n_tile * (kBN / 2)) * 2;
-    const int ncols = min(kBN / 2, p.N - n_tile * (kBN / 2));
-#pragma unroll
-    for (int mm = 0; mm < kSmallRows * kCpr / kNT; ++mm) {
-      const int c = etid + kNT * mm;
-      const int row = c / kCpr, ch = c % kCpr;
-      if (row < rows && ch * 8 < ncols)
-        *(bf16x8*)(Ht + (uint32_t)(row * (int)p.ldc + ch * 8) * 2u) =
-            *(const bf16x8*)(Eh + row * kLdH + ch * 8);
-    }
-  } else if constexpr (EPI == EPI_STORE) {
-    constexpr int kLdE = kBN + 4;  // 16 rows x 256 columns per pass, 1040-byte rows
-    float* E = (float*)stg;
-    float sc = 1.0f, inv = 1.0f;
-    if (p.c_scale) {
-      float* tmax = (float*)(stg + 32 * 1024);
-      float mx = 0.0f;
-      if constexpr (MI > 0) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[0][j][r]));
-      }
-      mx = wave_max_abs(mx);
-      if ((etid & 63) == 0) tmax[wave] = mx;
-      lds_barrier();
-      mx = tmax[0];
-#pragma unroll
-      for (int w = 1; w < kNW; ++w) mx = fmaxf(mx, tmax[w]);
-      f16_block_scale(mx, &sc, &inv);
-    }
-    char* Ct = (char*)p.C + ((int64_t)row_start * p.ldc + n_tile * kBN) * 4;
-    char* Ch = (char*)p.C + ((int64_t)row_start * p.ldc + n_tile * kBN) * 2;
-    const float* rs = p.row_scale ? p.row_scale + row_start : nullptr;
-    const int ncols = min(kBN, p.N - n_tile * kBN);
-    constexpr int kCpr = kBN / 4;  // 16-byte chunks per fp32 row
-#pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int prow0 = block_row0(pass, mi_hi, mi_lo);
-      const int pmi = pass < 2 ? mi_hi : mi_lo;
-      if (pmi > 0 && prow0 < rows) {  // uniform
-        if constexpr (MI > 0) {
-          if (wm == pass) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                E[(elk * 4 + r) * kLdE + wn * 128 + j * 16 + elr] = acc[0][j][r];
-          }
-        }
-        lds_barrier();
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {  // 16 rows of kCpr chunks, one row per wave
-          const int c = etid + kNT * mm;
-          const int lrow = c / kCpr, col = (c % kCpr) * 4;
-          const int row = prow0 + lrow;
-          if (p.c_scale) {
-            const f32x4 v = *(const f32x4*)(E + lrow * kLdE + col);
-            if (row < rows) {
-              if (col < ncols) {
-                const f16x4 h = {(_Float16)(v[0] * sc), (_Float16)(v[1] * sc),
-                                 (_Float16)(v[2] * sc), (_Float16)(v[3] * sc)};
-                *(f16x4*)(Ch + (uint32_t)(row * (int)p.ldc + col) * 2u) = h;
-              }
-              if ((etid & 63) == 0) p.c_scale[(int64_t)(row_start + row) * p.ldcs + n_tile] = inv;
-            }
-          } else if (row < rows && col < ncols) {
-            f32x4 v = *(const f32x4*)(E + lrow * kLdE + col);
-            if (rs) v *= rs[row];
-            *(f32x4*)(Ct + (uint32_t)(row * (int)p.ldc + col) * 4u) = v;
-          }
-        }
-        lds_barrier();
-      }
-    }
-  } else {  // EPI_ATOMIC_COMBINE
-    if constexpr (MI > 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wrow0 + elk * 4 + r;
-        if (row >= rows) continue;
-        const int a = p.perm[row_start + row];
-        const float w = p.topk_w[a];
-        float* dst = p.acc_out + (int64_t)(a / p.topk) * p.ldo;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int n = n_tile * kBN + wn * 128 + j * 16 + elr;
-          if (n < p.N) unsafeAtomicAdd(dst + n, w * acc[0][j][r]);
-        }
-      }
-    }
-  }
+  // ---- epilogue from registers, while the next tile's first stages land ----------------------
+  // The lane index is laundered through an empty asm so the store offsets are computed here,
+  // not hoisted out of the tile loop into registers (and spilled).
+  int elane = lane;
+  asm volatile("" : "+v"(elane));
+  if constexpr (MI > 0)
+    store_tile<MI, EPI, RS>(p, acc, elane, wn, wrow0, cur.row_start, rows, cur.n_tile);
 }
 
-template <int EPI>
+// Persistent, XCD-aware work-groups over the logical tiles: XCD x (work-groups b with
+// b % 8 == x) takes the x-th eighth of the tiles, its work-groups striding through it.
+// AROWS = 256 rows per token-row stage (any tile), or 64 when no tile has more than 64 rows
+// (decode batches: 8 KiB stages); RS: the STORE epilogue multiplies by row_scale.
+template <int EPI, int AROWS, bool RS>
 __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-mfma_small_kernel(const GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem[kLds];
+mfma_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSA * AROWS * kRow + kSB * kBStage];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int BNE = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
+  constexpr int BNE = EPI == EPI_SWIGLU ? kBN / 2 : kBN;  // output columns per tile
   const int ntN = (p.N + BNE - 1) / BNE;
   const int mt_total = p.tiles ? load_uniform(p.tile_count, 0) : (p.M + kBM - 1) / kBM;
   const int nt = mt_total * ntN;
   const int xcd = blockIdx.x % kXcds, per = gridDim.x / kXcds, jb = blockIdx.x / kXcds;
   const int lo = (int)((int64_t)nt * xcd / kXcds), hi = (int)((int64_t)nt * (xcd + 1) / kXcds);
-  const int ns = p.Kdim / 64;
+  const int ns = p.Kdim / 64;  // DMA stages (Kdim is a multiple of 64)
 
-  // The next tile's first three stages come with this tile's last three refills, which needs
-  // three stages per tile; shorter reductions run each tile with its own prologue.
+  // The next tile's stages 0-2 come with this tile's last three refills, which needs three
+  // stages per tile; shorter reductions run each tile with its own prologue.  A tile's map
+  // entry comes from the previous tile, which needed it for those refills (first tile: here).
   const bool cross = ns >= 3;
+  int t = lo + jb;
+  TileMap cur, nx;
+  if (t < hi) load_map(p, t, ntN, mt_total, cur);
   int G0 = 0;
-  for (int t = lo + jb; t < hi; t += per) {
-    int group, row_start, rows, n_tile;
-    decode_mtile(p, t, ntN, mt_total, &group, &row_start, &rows, &n_tile);
-    int nx_group = -1, nx_row_start = 0, nx_rows = 1, nx_n_tile = 0, nx_mi = 0;
-    if (cross && t + per < hi) {
-      decode_mtile(p, t + per, ntN, mt_total, &nx_group, &nx_row_start, &nx_rows, &nx_n_tile);
-      nx_mi = wave < 4 ? 1 : (nx_rows > 32 ? 1 : 0);
-    }
-    const int mi_hi = 1, mi_lo = rows > 32 ? 1 : 0;  // rows <= 64 (the host guarantees it)
+  for (; t < hi; t += per) {
+    const int tn = cross && t + per < hi ? t + per : -1;
+    int mi_hi, mi_lo;
+    tile_mi(cur.rows, &mi_hi, &mi_lo);
     const bool pre = cross && G0 > 0;
-    if (wave < 4 || mi_lo)
-      small_tile<1, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns, mi_hi, mi_lo, G0,
-                         pre, nx_group, nx_row_start, nx_rows, nx_n_tile, nx_mi);
-    else
-      small_tile<0, EPI>(p, smem, tid, wave, group, row_start, rows, n_tile, ns, mi_hi, mi_lo, G0,
-                         pre, nx_group, nx_row_start, nx_rows, nx_n_tile, nx_mi);
+    const auto run = [&](auto mi) {
+      ring_tile<decltype(mi)::value, EPI, AROWS, RS>(p, smem, tid, wave, cur, ns, mi_hi, mi_lo,
+                                                     G0, pre, tn, ntN, mt_total, nx);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    const int mi = wave < 4 ? mi_hi : mi_lo;  // waves 0-3 hold row blocks 0 and 1
+    if constexpr (AROWS == 64) {
+      if (mi == 0) run(I0{}); else run(I1{});
+    } else {
+      switch (mi) {
+        case 0: run(I0{}); break;
+        case 1: run(I1{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        default: run(std::integral_constant<int, 4>{}); break;
+      }
+    }
     G0 += ns;
+    if (tn >= 0)
+      cur = nx;
+    else if (t + per < hi)
+      load_map(p, t + per, ntN, mt_total, cur);
   }
 }
+
+constexpr int kSmallRows = 64;  // token-row stage rows of the decode-batch variant
 
 template <int EPI>
 hipError_t launch_epi(const GemmParams& p, int64_t max_mtiles, hipStream_t stream) {
@@ -731,10 +627,21 @@ hipError_t launch_epi(const GemmParams& p, int64_t max_mtiles, hipStream_t strea
   if (grid < kXcds) grid = kXcds;
   const bool small = p.tiles ? (p.rows_bound > 0 && p.rows_bound <= kSmallRows)
                              : p.M <= kSmallRows;
-  if (small)
-    hipLaunchKernelGGL((mfma_small_kernel<EPI>), dim3((unsigned)grid), dim3(kNT), 0, stream, p);
-  else
-    hipLaunchKernelGGL((mfma_kernel<EPI>), dim3((unsigned)grid), dim3(kNT), 0, stream, p);
+  const dim3 g((unsigned)grid), b(kNT);
+  if constexpr (EPI == EPI_STORE) {
+    if (p.row_scale) {
+      if (small)
+        hipLaunchKernelGGL((mfma_kernel<EPI, kSmallRows, true>), g, b, 0, stream, p);
+      else
+        hipLaunchKernelGGL((mfma_kernel<EPI, kBM, true>), g, b, 0, stream, p);
+      return hipGetLastError();
+    }
+  }
+  if (small) {
+    hipLaunchKernelGGL((mfma_kernel<EPI, kSmallRows, false>), g, b, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((mfma_kernel<EPI, kBM, false>), g, b, 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -366,7 +366,10 @@ __global__ void __launch_bounds__(512) stream_kernel(const GemmParams p) {
                                    (_Float16)(v[2] * sc), (_Float16)(v[3] * sc)};
                   *(f16x4*)(Ch + (uint32_t)(row * (int)p.ldc + col) * 2u) = h;
                 }
-                if ((etid & 63) == 0) p.c_scale[(int64_t)(cur.row_start + row) * p.ldcs + cur.n_tile] = inv;
+                // the tile's factor for each of its kScaleCols-column blocks that holds columns
+                if ((etid & 63) < BN / kScaleCols && (etid & 63) * kScaleCols < ncols)
+                  p.c_scale[(int64_t)(cur.row_start + row) * p.ldcs +
+                            cur.n_tile * (BN / kScaleCols) + (etid & 63)] = inv;
               }
             } else if (row < cur.rows && col < ncols) {
               f32x4 v = *(const f32x4*)(E + lrow * kLdE + col);

@@ -27,6 +27,9 @@ enum Epilogue : int {
   EPI_ATOMIC_COMBINE = 2,  // out_acc[token(row), n] += w(row) * C[row, n]  (fp32 atomics)
 };
 
+// Columns per power-of-two factor of fp16 expert rows (GemmParams::c_scale, combine16).
+constexpr int kScaleCols = 128;
+
 struct GemmParams {
   // A operand: row r of the logical A matrix is A + arow(r) * lda_bytes.
   const char* A;
@@ -49,9 +52,9 @@ struct GemmParams {
   void* C;                  // STORE: fp32 [rows, ldc] (or fp16 with c_scale); SWIGLU: dtype
   int64_t ldc;
   float* c_scale;           // STORE, streaming and matrix-core GEMMs only: if set, C holds fp16
-                            // values scaled by a power of two per output tile (tile max
-                            // < 2^15), and c_scale[row * ldcs + n_tile] the factor that
-                            // restores row `row` of N tile n_tile (256 columns)
+                            // values scaled by a power of two per block of kScaleCols columns
+                            // of a row (block max < 2^15), and c_scale[row * ldcs + b] the
+                            // factor that restores block b of row `row`
   int64_t ldcs;
   float* C2;                // STORE: column N (if B2) -> C2[row]
   const float* col_bias;    // STORE: + col_bias[n]
@@ -173,7 +176,7 @@ hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const fl
                           const float* y_shared, const float* gate, int64_t T, int K, int D,
                           void* out, int out_dtype, hipStream_t stream);
 // The same combine over fp16 expert rows y16 [T*K, D] with block factors ysc [T*K, nblk]
-// (nblk = ceil(D / 256)); each term is (topk_w * factor) * value, summed in slot order.
+// (nblk = ceil(D / kScaleCols)); each term is (topk_w * factor) * value, summed in slot order.
 hipError_t launch_combine16(const void* y16, const float* ysc, int nblk, const int32_t* inv_perm,
                             const float* topk_w, const float* y_shared, const float* gate,
                             int64_t T, int K, int D, void* out, int out_dtype,
