@@ -3,13 +3,14 @@
 // that the expert runs once on all of them; "1.6 混合专家（MoE）" §二: route, group, compute,
 // merge).
 //
-// The assignments a = t*K + k are cut into segments of 1024 consecutive ids, one wave64 each
-// (each lane prefetches its 16 ids of the segment at once).
+// The assignments a = t*K + k are cut into segments of 512 consecutive ids, one wave64 each
+// (each lane prefetches its 8 ids of the segment at once).
 //   count        : each wave histograms its segment in LDS (atomics are fine: counts do not
 //                  depend on order) and writes seg_counts[segment][E].
 //   scan_scatter : every work-group re-derives the expert totals, offsets and its segments'
-//                  first ranks from seg_counts (work-group 0 also writes counts, offsets and
-//                  the tile maps); then each wave re-reads its segment 64 ids at a time and
+//                  first ranks from seg_counts (work-group 0 also writes counts and offsets,
+//                  an extra last work-group the tile maps); then each wave re-reads its
+//                  segment 64 ids at a time and
 //                  places every assignment by its ballot-computed rank.  Segments, rounds and
 //                  lanes all follow ascending a, so the sort is stable and the result
 //                  bit-exact.
@@ -26,7 +27,7 @@ namespace moe {
 namespace {
 
 constexpr int kScanThreads = 1024;
-constexpr int kSegRounds = 16;               // 64-id rounds per segment
+constexpr int kSegRounds = 8;                // 64-id rounds per segment
 constexpr int kSegLen = 64 * kSegRounds;      // assignments per segment (one wave)
 // Single-work-group dispatch up to this many assignments (its LDS holds 18 ints per expert).
 constexpr int64_t kFusedMaxA = 8192;
@@ -155,14 +156,15 @@ __global__ void __launch_bounds__(kScanThreads) tile_map_kernel(const int32_t* _
 // Scan and scatter in one launch.  Work-group b owns segments [8 b, 8 b + 8), one per wave.
 // Every work-group first re-derives, from the per-segment histograms, each expert's total
 // (capped at the capacity) and the first rank of its own segments within the expert; the
-// histograms are a few KiB per hundred segments, read from L2.  Work-group 0 also writes the
-// counts, offsets and tile maps.  Then each wave re-reads its segment 64 ids at a time: lanes
+// histograms are a few KiB per hundred segments, read from L2 in one batch of loads.
+// Work-group 0 also writes the counts and offsets; with a tile map, one more work-group (the
+// last, which owns no segment) builds it.  Then each wave re-reads its segment 64 ids at a time: lanes
 // holding the same expert find each other with one ballot per bit of the expert id, and a
 // lane's rank among its lower-numbered peers plus its expert's running rank (in LDS) is its
 // rank q within the expert; offsets[e] + q is its position, unless q reaches the capacity.
 constexpr int kSSThreads = 512;
 constexpr int kSSWaves = kSSThreads / 64;
-constexpr int kSSBatch = 8;  // histogram rows loaded together
+constexpr int kSSBatch = 64;  // histogram rows loaded together
 
 __global__ void __launch_bounds__(kSSThreads) scan_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t A, int E, int nbits, int cap, int64_t nseg,
@@ -210,7 +212,12 @@ __global__ void __launch_bounds__(kSSThreads) scan_scatter_kernel(
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) offsets[E] = total;
   __syncthreads();
-  if (blockIdx.x == 0 && tiles) build_tiles<kSSThreads>(cnt, off, E, ts, scratch, tiles, tile_count);
+  // the tile maps come from the extra last work-group, which owns no segment, so that no
+  // scatter waits for them
+  if (tiles && blockIdx.x == gridDim.x - 1) {
+    build_tiles<kSSThreads>(cnt, off, E, ts, scratch, tiles, tile_count);
+    return;
+  }
 
   const int64_t seg = seg0 + wave;
   if (seg >= nseg) return;  // after every work-group barrier
@@ -408,8 +415,8 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_co
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const size_t lds = (size_t)((kSSWaves + 2) * E + 32) * sizeof(int);
-  hipLaunchKernelGGL(scan_scatter_kernel, dim3((unsigned)((nseg + kSSWaves - 1) / kSSWaves)),
-                     dim3(kSSThreads), lds, stream, idx, A, E, nbits, cap, nseg, seg_counts,
+  const unsigned groups = (unsigned)((nseg + kSSWaves - 1) / kSSWaves) + (tiles ? 1 : 0);
+  hipLaunchKernelGGL(scan_scatter_kernel, dim3(groups), dim3(kSSThreads), lds, stream, idx, A, E, nbits, cap, nseg, seg_counts,
                      counts, offsets, perm, inv_perm, ts, tiles, tile_count);
   return hipGetLastError();
 }
