@@ -26,10 +26,12 @@
 //    three or more K stages the rings run on across a work-group's tiles: a tile's last
 //    refills fetch the next tile's first stages.
 //  * Epilogues store straight from the accumulators, which hold the transposed tile (weights
-//    are the MFMA's first operand), so each lane writes 4 consecutive columns of a row: fused
-//    SiLU·up (a wave's 8 column tiles are 4 gate/up pairs), fp32 with an optional row scale,
-//    fp16 with a power-of-two factor per row and 128-column block, or the weighted fp32
-//    atomic combine.  No LDS is involved, so the next tile's loads fly meanwhile.
+//    are the MFMA's first operand), so each lane owns consecutive columns of a row: 8 for the
+//    fused SiLU·up (a wave's 8 column tiles are 4 gate/up pairs) and fp16 rows with a
+//    power-of-two factor per row and 128-column block, whose weight rows are read in a paired
+//    order (boff) so that each 16-byte store fills 64 bytes of a row; 4 for fp32 rows (optional
+//    row scale) and the weighted fp32 atomic combine.  No LDS is involved, so the next tile's
+//    loads fly meanwhile.
 #include <type_traits>
 
 #include "kernels.h"
@@ -66,6 +68,11 @@ __device__ __forceinline__ void barrier_after() {
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
+// Weight-row swizzle of the paired column layout (see boff): bits 1, 3 and 4 of the row, which
+// tell apart the 16 rows that one fragment read takes (rows 8 q + s, q, s < 4, plus a multiple
+// of 4 that only sets bit 2 or bits above 4), so that read is conflict-free as well.
+__device__ __forceinline__ int swz_pair(int row) { return ((row >> 1) & 1) | (((row >> 3) & 3) << 1); }
+
 // Barrier for LDS traffic only: waits for this wave's LDS operations and leaves its
 // vector-memory operations (stores, prefetches) in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -88,20 +95,30 @@ __device__ __forceinline__ void dma_operand(const char* base, const uint32_t* sr
 }
 
 // Fragment u of this wave in a stage: A fragments 0..7 (16 rows each) at la + 1024 u, B
-// fragments at lb + boff(j).  Every fragment row has the same (row >> 1) & 3, so one swizzled
-// lane offset per operand serves all of them and the rest is an immediate offset.
-template <bool SWIGLU>
+// fragments at lb + boff(j).  Every fragment row has the same swizzle, so one swizzled lane
+// offset per operand serves all of them and the rest is an immediate offset.
+//
+// B column tiles: output columns of MFMA tile j, lane row c (c = 4 lk + r holds column 4 lk + r
+// of the transposed accumulator).  Plain layout: columns 16 j + c.  Paired layout (PAIR): tiles
+// 2m and 2m + 1 interleave in groups of 4, column 32 m + 8 (c / 4) + 4 (j & 1) + c % 4, so the
+// lane with lk holds columns 32 m + 8 lk + [0, 8) across the pair: 16-byte stores of 8 bf16 or
+// fp16 values, 64-byte row runs per store.  The lane's row offset is then 8 (lr / 4) + lr % 4
+// and tile j adds 32 (j / 2) + 4 (j & 1).  For SwiGLU, tiles j and j + 4 are a gate/up pair
+// (gate rows first, up rows from kBN / 2), with the same layout over j & 3.
+template <bool SWIGLU, bool PAIR>
 __device__ __forceinline__ int boff(int j) {
-  return SWIGLU ? ((j < 4 ? 0 : kBN / 2) + (j & 3) * 16) * kRow : j * 16 * kRow;
+  const int jj = SWIGLU ? (j & 3) : j;
+  const int col = PAIR ? 32 * (jj >> 1) + 4 * (jj & 1) : 16 * jj;
+  return ((SWIGLU && j >= 4 ? kBN / 2 : 0) + col) * kRow;
 }
 
-template <int MI, bool SWIGLU>
+template <int MI, bool SWIGLU, bool PAIR>
 __device__ __forceinline__ void read_frags(const char* la, const char* lb, bf16x8* af,
                                            bf16x8* bfr) {
 #pragma unroll
   for (int i = 0; i < MI; ++i) af[i] = *(const bf16x8*)(la + i * 16 * kRow);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) bfr[j] = *(const bf16x8*)(lb + boff<SWIGLU>(j));
+  for (int j = 0; j < 8; ++j) bfr[j] = *(const bf16x8*)(lb + boff<SWIGLU, PAIR>(j));
 }
 
 // The 8·MI MFMAs of one 32-wide K step, reading the next step's fragments in between: one of
@@ -110,7 +127,7 @@ __device__ __forceinline__ void read_frags(const char* la, const char* lb, bf16x
 // each 16 x 16 accumulator holds the transposed output tile: lane (lr, lk) gets token row lr,
 // output columns 4 lk + [0, 4) (both operands have the same fragment layout, so the swap is
 // free and lets the epilogue store 4 consecutive columns per lane).
-template <int MI, bool SWIGLU>
+template <int MI, bool SWIGLU, bool PAIR>
 __device__ __forceinline__ void mma_stage(f32x4 (*acc)[8], bf16x8* af, const bf16x8* bfr,
                                           const char* la_n, const char* lb_n, bf16x8* bfr_n) {
 #pragma unroll
@@ -120,7 +137,7 @@ __device__ __forceinline__ void mma_stage(f32x4 (*acc)[8], bf16x8* af, const bf1
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
       if ((i * 8 + j + 1) % MI == 0) {
         const int b = (i * 8 + j + 1) / MI - 1;
-        bfr_n[b] = *(const bf16x8*)(lb_n + boff<SWIGLU>(b));
+        bfr_n[b] = *(const bf16x8*)(lb_n + boff<SWIGLU, PAIR>(b));
       }
     }
     af[i] = *(const bf16x8*)(la_n + i * 16 * kRow);
@@ -189,10 +206,12 @@ __device__ __forceinline__ int lane_chunk(int lane, int wave) {
   return (lane & 7) ^ swz(8 * wave + (lane >> 3));
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, bool PAIR>
 __device__ __forceinline__ void weight_sources(const GemmParams& p, int lane, int wave,
                                                int n_tile, uint32_t* sb) {
-  const int chunk = lane_chunk(lane, wave);
+  // staged row r = 8 (wave + 8 i) + (lane >> 3): bits 1, 3 and 4 do not depend on i either
+  const int r0 = 8 * wave + (lane >> 3);
+  const int chunk = (lane & 7) ^ (PAIR ? swz_pair(r0) : swz(r0));
 #pragma unroll
   for (int i = 0; i < kDma; ++i) {
     const int r = 8 * (wave + kNW * i) + (lane >> 3);
@@ -262,10 +281,10 @@ __device__ __forceinline__ void load_map(const GemmParams& p, int t, int ntN, in
 
 // Every DMA source of a tile: weight rows, and token rows of the first NA instructions (the
 // gathered ones in one round of loads).
-template <bool SWIGLU, int NA>
+template <bool SWIGLU, bool PAIR, int NA>
 __device__ __forceinline__ void tile_sources(const GemmParams& p, int lane, int wave,
                                              const TileMap& tile, uint32_t* sa, uint32_t* sb) {
-  weight_sources<SWIGLU>(p, lane, wave, tile.n_tile, sb);
+  weight_sources<SWIGLU, PAIR>(p, lane, wave, tile.n_tile, sb);
   if (p.a_gather) {
     int v[NA][8];
 #pragma unroll
@@ -290,18 +309,23 @@ __device__ __forceinline__ void dma_rows_n(int n, const char* base, const uint32
 }
 
 // Epilogue straight from the accumulators.  The weight fragment is the MFMA's first operand,
-// so lane (lr, lk) of MFMA tile (i, j) holds row wrow0 + 16 i + lr of the output tile and
-// columns 16 j + 4 lk + [0, 4) of its wave's column block: every lane writes 4 consecutive
-// columns of one row, and an MFMA tile leaves as 16 row runs of 32 (bf16, fp16) or 64 (fp32)
-// bytes that L2 merges with the neighbouring tiles' into whole lines.  No LDS, no barrier.
-template <int MI, int EPI, bool RS>
+// so lane (lr, lk) of MFMA tile (i, j) holds row wrow0 + 16 i + lr of the output tile and 4
+// consecutive columns of its wave's column block (boff): in the plain layout columns
+// 16 j + 4 lk + [0, 4) (fp32 rows and the atomic combine: 16-byte stores, 64-byte row runs),
+// in the paired layout columns 32 m + 8 lk + [0, 8) over tiles j = 2m, 2m + 1 (bf16 H and
+// fp16 rows: 16-byte stores, 64-byte row runs, half the store instructions).  L2 merges the
+// runs into whole lines.  No LDS, no barrier.
+template <int MI, int EPI, bool RS, bool PAIR>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x4 (*acc)[8], int lane,
                                            int wn, int wrow0, int row_start, int rows,
                                            int n_tile) {
-  const int lr = lane & 15, c4 = (lane >> 4) * 4;
+  typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  const int lr = lane & 15, lk = lane >> 4;
   if constexpr (EPI == EPI_SWIGLU) {
-    // H: the tile's 128 columns; wave wn holds [64 wn, +64) as gate tiles j and up tiles j + 4
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    static_assert(PAIR, "SwiGLU rows use the paired layout");
+    // H: the tile's 128 columns; wave wn holds [64 wn, +64) as gate tiles j and up tiles j + 4,
+    // 8 consecutive columns per lane
     const int ncols = min(kBN / 2, p.N - n_tile * (kBN / 2));
     __bf16* Ht = (__bf16*)p.C + (int64_t)row_start * p.ldc + n_tile * (kBN / 2);
 #pragma unroll
@@ -309,78 +333,87 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x4 (*ac
       const int row = wrow0 + 16 * i + lr;
       if (row < rows) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = wn * 64 + 16 * j + c4;
+        for (int m = 0; m < 2; ++m) {
+          const int col = wn * 64 + 32 * m + 8 * lk;
           if (col < ncols) {
-            bf16x4 h;
+            bf16x8v h;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              h[r] = (__bf16)(silu_fast(acc[i][j][r]) * acc[i][j + 4][r]);
-            *(bf16x4*)(Ht + (int64_t)row * p.ldc + col) = h;
+            for (int r = 0; r < 4; ++r) {
+              h[r] = (__bf16)(silu_fast(acc[i][2 * m][r]) * acc[i][2 * m + 4][r]);
+              h[4 + r] = (__bf16)(silu_fast(acc[i][2 * m + 1][r]) * acc[i][2 * m + 5][r]);
+            }
+            *(bf16x8v*)(Ht + (int64_t)row * p.ldc + col) = h;
           }
         }
       }
     }
-  } else if constexpr (EPI == EPI_STORE) {
-    static_assert(kScaleCols == kBN / 2, "one fp16 factor block per wave column half");
+  } else if constexpr (EPI == EPI_STORE && PAIR) {
+    // fp16 with a power-of-two factor per row of the wave's 128 columns, from the row's largest
+    // |value| (the lane's 32 values, then the 4 lanes that share the row)
+    static_assert(kScaleCols == kBN / 2 && !RS, "one fp16 factor block per wave column half");
     const int ncols = min(kBN, p.N - n_tile * kBN);
     const int c0 = wn * 128;  // this wave's columns [c0, c0 + 128) of the tile
-    if (p.c_scale) {
-      // fp16 with a power-of-two factor per row of the wave's 128 columns, from the row's
-      // largest |value| (the lane's 32 values, then the 4 lanes that share the row)
-      _Float16* Ch = (_Float16*)p.C + (int64_t)row_start * p.ldc + n_tile * kBN;
+    _Float16* Ch = (_Float16*)p.C + (int64_t)row_start * p.ldc + n_tile * kBN;
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        float mx = 0.0f;
+    for (int i = 0; i < MI; ++i) {
+      float mx = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (c0 + 16 * j < ncols)
+      for (int j = 0; j < 8; ++j)
+        if (c0 + 32 * (j >> 1) < ncols)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[i][j][r]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        float sc, inv;
-        f16_block_scale(mx, &sc, &inv);
-        const int row = wrow0 + 16 * i + lr;
-        if (row < rows && c0 < ncols) {
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[i][j][r]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      float sc, inv;
+      f16_block_scale(mx, &sc, &inv);
+      const int row = wrow0 + 16 * i + lr;
+      if (row < rows && c0 < ncols) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int col = c0 + 16 * j + c4;
-            if (col < ncols) {
-              const f16x4 h = {(_Float16)(acc[i][j][0] * sc), (_Float16)(acc[i][j][1] * sc),
-                               (_Float16)(acc[i][j][2] * sc), (_Float16)(acc[i][j][3] * sc)};
-              *(f16x4*)(Ch + (int64_t)row * p.ldc + col) = h;
+        for (int m = 0; m < 4; ++m) {
+          const int col = c0 + 32 * m + 8 * lk;
+          if (col < ncols) {
+            f16x8 h;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              h[r] = (_Float16)(acc[i][2 * m][r] * sc);
+              h[4 + r] = (_Float16)(acc[i][2 * m + 1][r] * sc);
             }
+            *(f16x8*)(Ch + (int64_t)row * p.ldc + col) = h;
           }
-          if (lane < 16)
-            p.c_scale[(int64_t)(row_start + row) * p.ldcs + n_tile * (kBN / kScaleCols) + wn] =
-                inv;
         }
+        if (lane < 16)
+          p.c_scale[(int64_t)(row_start + row) * p.ldcs + n_tile * (kBN / kScaleCols) + wn] = inv;
       }
-    } else {
-      // fp32, times row_scale[row] in the RS variant (its vector load is waited for at once,
-      // which also waits for the next tile's first stages; the variant serves only the
-      // row-scaled shared expert)
-      float* Ct = (float*)p.C + (int64_t)row_start * p.ldc + n_tile * kBN;
+    }
+  } else if constexpr (EPI == EPI_STORE) {
+    // fp32, times row_scale[row] in the RS variant (its vector load is waited for at once,
+    // which also waits for the next tile's first stages; the variant serves only the
+    // row-scaled shared expert)
+    static_assert(!PAIR, "fp32 rows use the plain layout");
+    const int c4 = 4 * lk;
+    const int ncols = min(kBN, p.N - n_tile * kBN);
+    const int c0 = wn * 128;
+    float* Ct = (float*)p.C + (int64_t)row_start * p.ldc + n_tile * kBN;
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int row = wrow0 + 16 * i + lr;
-        if (row < rows) {
-          float s = 1.0f;
-          if constexpr (RS) s = p.row_scale[row_start + row];
+    for (int i = 0; i < MI; ++i) {
+      const int row = wrow0 + 16 * i + lr;
+      if (row < rows) {
+        float s = 1.0f;
+        if constexpr (RS) s = p.row_scale[row_start + row];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int col = c0 + 16 * j + c4;
-            if (col < ncols) {
-              f32x4 v = acc[i][j];
-              if constexpr (RS) v *= s;
-              *(f32x4*)(Ct + (int64_t)row * p.ldc + col) = v;
-            }
+        for (int j = 0; j < 8; ++j) {
+          const int col = c0 + 16 * j + c4;
+          if (col < ncols) {
+            f32x4 v = acc[i][j];
+            if constexpr (RS) v *= s;
+            *(f32x4*)(Ct + (int64_t)row * p.ldc + col) = v;
           }
         }
       }
     }
   } else {  // EPI_ATOMIC_COMBINE: the token's output row += routing weight * row
+    static_assert(!PAIR, "the atomic combine uses the plain layout");
+    const int c4 = 4 * lk;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int row = wrow0 + 16 * i + lr;
@@ -417,7 +450,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x4 (*ac
 // describe it, nx_group < 0 if there is none, and nx_mi is this wave's MI there), and that
 // tile then starts with them in flight or landed (`pre`), so the weight stream does not stop
 // for an epilogue or a prologue.
-template <int MI, int EPI, int AROWS, bool RS>
+template <int MI, int EPI, int AROWS, bool RS, bool PAIR>
 __device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int tid, int wave,
                                           const TileMap& cur, int ns, int mi_hi, int mi_lo,
                                           int G0, bool pre, int tn, int ntN, int mt_total,
@@ -441,12 +474,16 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int t
   // the matching up rows, and a wave's column tiles j and j + 4 are a gate/up pair.
   const int wrow0 = block_row0(wm, mi_hi, mi_lo);
   const int la_row = (wrow0 + lr) * kRow;
-  const int lb_row = ((kSwiglu ? wn * 64 : wn * 128) + lr) * kRow;
   const int ch0 = (lk ^ swz(lr)) << 4, ch1 = ((4 + lk) ^ swz(lr)) << 4;
+  // B: the lane's fragment row within its column tiles (boff) and that row's swizzle
+  const int lrow = PAIR ? 8 * (lr >> 2) + (lr & 3) : lr;
+  const int lb_row = ((kSwiglu ? wn * 64 : wn * 128) + lrow) * kRow;
+  const int bsw = PAIR ? swz_pair(lrow) : swz(lrow);
+  const int cb0 = (lk ^ bsw) << 4, cb1 = ((4 + lk) ^ bsw) << 4;
 
   const int rows = cur.rows;
   uint32_t srcA[kMaxMI], srcB[kDma], nsA[kMaxMI], nsB[kDma];
-  tile_sources<kSwiglu, kMaxMI>(p, lane, wave, cur, srcA, srcB);
+  tile_sources<kSwiglu, PAIR, kMaxMI>(p, lane, wave, cur, srcA, srcB);
   const char* gbase = p.B + (int64_t)cur.group * p.b_group_bytes;
 
   // The next tile (logical tile tn >= 0), whose first stages this tile's last refills fetch:
@@ -455,7 +492,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int t
   int nx_mi = 0;  // this wave's token-row DMA instructions per stage of the next tile
   if (nxt) {
     load_map(p, tn, ntN, mt_total, nx);
-    tile_sources<kSwiglu, kMaxMI>(p, lane, wave, nx, nsA, nsB);
+    tile_sources<kSwiglu, PAIR, kMaxMI>(p, lane, wave, nx, nsA, nsB);
     int nh, nl;
     tile_mi(nx.rows, &nh, &nl);
     nx_mi = wave < 4 ? nh : nl;
@@ -495,7 +532,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int t
   // between two sets)
   bf16x8 af0[MIA], bf0[8], bf1[8];
   if constexpr (MI > 0)
-    read_frags<MI, kSwiglu>(a_at(G0) + la_row + ch0, b_at(G0) + lb_row + ch0, af0, bf0);
+    read_frags<MI, kSwiglu, PAIR>(a_at(G0) + la_row + ch0, b_at(G0) + lb_row + cb0, af0, bf0);
 
   // Stage g's MFMAs: first half (step 2g) while reading the second half's fragments from the
   // same stage; then publish stage g+1 (this wave's copies landed; every wave has read all of
@@ -508,22 +545,22 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int t
   for (; g + 3 < ns; ++g) {  // refills of this tile only
     const int ra1 = ra ^ 1, rb1 = rb == 2 ? 0 : rb + 1;
     if constexpr (MI > 0)
-      mma_stage<MI, kSwiglu>(acc, af0, bf0, sA + ra * kAS + la_row + ch1,
-                             sB + rb * kBStage + lb_row + ch1, bf1);
+      mma_stage<MI, kSwiglu, PAIR>(acc, af0, bf0, sA + ra * kAS + la_row + ch1,
+                             sB + rb * kBStage + lb_row + cb1, bf1);
     barrier_after<kDma, 0>();  // B(g+2) went out after A(g+1) and may still fly
     dma_operand<kNW, MI>(p.A, srcA, (uint32_t)(g + 2) * kRow, sA + ra * kAS, wave);
     dma_operand<kNW>(gbase, srcB, (uint32_t)(g + 3) * kRow, sB + rb * kBStage, wave);
     if constexpr (MI > 0)
-      mma_stage<MI, kSwiglu>(acc, af0, bf1, sA + ra1 * kAS + la_row + ch0,
-                             sB + rb1 * kBStage + lb_row + ch0, bf0);
+      mma_stage<MI, kSwiglu, PAIR>(acc, af0, bf1, sA + ra1 * kAS + la_row + ch0,
+                             sB + rb1 * kBStage + lb_row + cb0, bf0);
     ra = ra1;
     rb = rb1;
   }
   for (; g < ns; ++g) {  // the last three stages
     const int ra1 = ra ^ 1, rb1 = rb == 2 ? 0 : rb + 1;
     if constexpr (MI > 0)
-      mma_stage<MI, kSwiglu>(acc, af0, bf0, sA + ra * kAS + la_row + ch1,
-                             sB + rb * kBStage + lb_row + ch1, bf1);
+      mma_stage<MI, kSwiglu, PAIR>(acc, af0, bf0, sA + ra * kAS + la_row + ch1,
+                             sB + rb * kBStage + lb_row + cb1, bf1);
     if (g + 1 < ns) {
       if (g + 2 < ns || nxt)  // B(g+2) went out after A(g+1) and may still fly
         barrier_after<kDma, 0>();
@@ -542,8 +579,8 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int t
     if constexpr (MI > 0) {
       // after the last stage these reads fetch unused leftovers
       const int na = g + 1 < ns ? ra1 : ra, nb = g + 1 < ns ? rb1 : rb;
-      mma_stage<MI, kSwiglu>(acc, af0, bf1, sA + na * kAS + la_row + ch0,
-                             sB + nb * kBStage + lb_row + ch0, bf0);
+      mma_stage<MI, kSwiglu, PAIR>(acc, af0, bf1, sA + na * kAS + la_row + ch0,
+                             sB + nb * kBStage + lb_row + cb0, bf0);
     }
     ra = ra1;
     rb = rb1;
@@ -555,14 +592,15 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int t
   int elane = lane;
   asm volatile("" : "+v"(elane));
   if constexpr (MI > 0)
-    store_tile<MI, EPI, RS>(p, acc, elane, wn, wrow0, cur.row_start, rows, cur.n_tile);
+    store_tile<MI, EPI, RS, PAIR>(p, acc, elane, wn, wrow0, cur.row_start, rows, cur.n_tile);
 }
 
 // Persistent, XCD-aware work-groups over the logical tiles: XCD x (work-groups b with
 // b % 8 == x) takes the x-th eighth of the tiles, its work-groups striding through it.
 // AROWS = 256 rows per token-row stage (any tile), or 64 when no tile has more than 64 rows
-// (decode batches: 8 KiB stages); RS: the STORE epilogue multiplies by row_scale.
-template <int EPI, int AROWS, bool RS>
+// (decode batches: 8 KiB stages); RS: the STORE epilogue multiplies by row_scale; PAIR: the
+// paired column layout (SwiGLU and fp16 rows, see boff).
+template <int EPI, int AROWS, bool RS, bool PAIR>
 __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mfma_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[kSA * AROWS * kRow + kSB * kBStage];
@@ -590,7 +628,7 @@ mfma_kernel(const GemmParams p) {
     tile_mi(cur.rows, &mi_hi, &mi_lo);
     const bool pre = cross && G0 > 0;
     const auto run = [&](auto mi) {
-      ring_tile<decltype(mi)::value, EPI, AROWS, RS>(p, smem, tid, wave, cur, ns, mi_hi, mi_lo,
+      ring_tile<decltype(mi)::value, EPI, AROWS, RS, PAIR>(p, smem, tid, wave, cur, ns, mi_hi, mi_lo,
                                                      G0, pre, tn, ntN, mt_total, nx);
     };
     using I0 = std::integral_constant<int, 0>;
@@ -628,19 +666,29 @@ hipError_t launch_epi(const GemmParams& p, int64_t max_mtiles, hipStream_t strea
   const bool small = p.tiles ? (p.rows_bound > 0 && p.rows_bound <= kSmallRows)
                              : p.M <= kSmallRows;
   const dim3 g((unsigned)grid), b(kNT);
-  if constexpr (EPI == EPI_STORE) {
-    if (p.row_scale) {
-      if (small)
-        hipLaunchKernelGGL((mfma_kernel<EPI, kSmallRows, true>), g, b, 0, stream, p);
-      else
-        hipLaunchKernelGGL((mfma_kernel<EPI, kBM, true>), g, b, 0, stream, p);
-      return hipGetLastError();
-    }
-  }
-  if (small) {
-    hipLaunchKernelGGL((mfma_kernel<EPI, kSmallRows, false>), g, b, 0, stream, p);
+  // layout and epilogue variants: SwiGLU and fp16 rows paired, fp32 rows (optionally
+  // row-scaled) and the atomic combine plain
+  const auto go = [&](auto rs, auto pair) {
+    constexpr bool RS = decltype(rs)::value, PAIR = decltype(pair)::value;
+    if (small)
+      hipLaunchKernelGGL((mfma_kernel<EPI, kSmallRows, RS, PAIR>), g, b, 0, stream, p);
+    else
+      hipLaunchKernelGGL((mfma_kernel<EPI, kBM, RS, PAIR>), g, b, 0, stream, p);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if constexpr (EPI == EPI_SWIGLU) {
+    go(F_{}, T_{});
+  } else if constexpr (EPI == EPI_STORE) {
+    if (p.c_scale && p.row_scale) return hipErrorInvalidValue;  // no row-scaled fp16 rows
+    if (p.c_scale)
+      go(F_{}, T_{});
+    else if (p.row_scale)
+      go(T_{}, F_{});
+    else
+      go(F_{}, F_{});
   } else {
-    hipLaunchKernelGGL((mfma_kernel<EPI, kBM, false>), g, b, 0, stream, p);
+    go(F_{}, F_{});
   }
   return hipGetLastError();
 }
