@@ -28,13 +28,31 @@ __device__ __forceinline__ float key_value(uint32_t o) {
   return __uint_as_float(u);
 }
 
+// One DPP step of a 64-bit wave max: v and the lane's DPP partner's value (rows outside
+// ROW_MASK keep their own).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ unsigned long long max_dpp_u64(unsigned long long v) {
+  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false);
+  const unsigned long long o = ((unsigned long long)ohi << 32) | olo;
+  return o > v ? o : v;
+}
+
+// Maximum over the wave, returned uniformly: DPP steps within quads (lane ^ 1, lane ^ 2), within
+// rows of 16 (half-mirror, mirror), then row 0's and 1's maxima carried into rows 1 and 3 and
+// row 1's into rows 2 and 3 (row broadcasts), leaving the wave's maximum in lane 63.  A max
+// does not depend on the order of its operands, so this is exact.
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const unsigned long long o = __shfl_xor(v, m, 64);
-    v = o > v ? o : v;
-  }
-  return v;
+  v = max_dpp_u64<0xB1, 0xf>(v);   // quad_perm [1, 0, 3, 2]
+  v = max_dpp_u64<0x4E, 0xf>(v);   // quad_perm [2, 3, 0, 1]
+  v = max_dpp_u64<0x141, 0xf>(v);  // row_half_mirror
+  v = max_dpp_u64<0x140, 0xf>(v);  // row_mirror
+  v = max_dpp_u64<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = max_dpp_u64<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((unsigned long long)hi << 32) | lo;
 }
 
 __device__ __forceinline__ float wave_max_f(float v) {
