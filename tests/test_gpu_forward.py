@@ -45,7 +45,7 @@ CASES = {
     # reduction lengths that are not a multiple of the streaming ring, ragged N tiles
     "odd_k": ("a3b_prefill", {"D": 192, "F": 320, "E": 16}, 300),
     # expert outputs far above the fp16 range (|y| ~ 1e5): the fp16 rows of the default path
-    # carry a power-of-two factor per 256-column block, so nothing overflows
+    # carry a power-of-two factor per row and 128-column block, so nothing overflows
     "huge_values": ("tiny", {"dtype": "bf16", "std_expert": 4.0, "D": 320}, 200),
     # batches of at most 64 tokens: reductions of exactly three K stages (the shortest that
     # carries the rings into the next tile) and of five, ragged N tiles, tiles over 32 rows
