@@ -29,7 +29,8 @@
 //    are the MFMA's first operand), so each lane owns consecutive columns of a row: 8 for the
 //    fused SiLU·up (a wave's 8 column tiles are 4 gate/up pairs) and fp16 rows with a
 //    power-of-two factor per row and 128-column block, whose weight rows are read in a paired
-//    order (boff) so that each 16-byte store fills 64 bytes of a row; 4 for fp32 rows (optional
+//    order (boff) so that each 16-byte store fills 64 bytes of a row (fp16 rows: neighbouring
+//    lanes trade a chunk, and each store fills whole 128-byte lines); 4 for fp32 rows (optional
 //    row scale) and the weighted fp32 atomic combine.  No LDS is involved, so the next tile's
 //    loads fly meanwhile.
 #include <type_traits>
@@ -366,24 +367,42 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x4 (*ac
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       float sc, inv;
       f16_block_scale(mx, &sc, &inv);
+      // Per 64-column span the lane holds two 8-column chunks of its row (pairs 2p and 2p + 1:
+      // columns 8 lk and 32 + 8 lk of the span).  Lanes lr and lr ^ 1 (rows R, R + 1) trade one
+      // chunk (DPP swap), so that one store writes row R's whole 128 bytes from the 8 lanes of
+      // the two rows and the next store row R + 1's: every store fills whole lines.
       const int row = wrow0 + 16 * i + lr;
-      if (row < rows && c0 < ncols) {
+      const bool odd = lr & 1;
+      const int row_a = row - (odd ? 1 : 0), row_b = row_a + 1;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int col = c0 + 32 * m + 8 * lk;
-          if (col < ncols) {
-            f16x8 h;
+      for (int sp = 0; sp < 2; ++sp) {
+        const int cs = c0 + 64 * sp;
+        if (cs < ncols) {  // uniform
+          f16x8 ca, cb;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              h[r] = (_Float16)(acc[i][2 * m][r] * sc);
-              h[4 + r] = (_Float16)(acc[i][2 * m + 1][r] * sc);
-            }
-            *(f16x8*)(Ch + (int64_t)row * p.ldc + col) = h;
+          for (int r = 0; r < 4; ++r) {
+            ca[r] = (_Float16)(acc[i][4 * sp][r] * sc);
+            ca[4 + r] = (_Float16)(acc[i][4 * sp + 1][r] * sc);
+            cb[r] = (_Float16)(acc[i][4 * sp + 2][r] * sc);
+            cb[4 + r] = (_Float16)(acc[i][4 * sp + 3][r] * sc);
           }
+          // row R's lane sends its second chunk, row R + 1's lane its first
+          typedef int i32x4 __attribute__((ext_vector_type(4)));
+          const i32x4 snd = odd ? __builtin_bit_cast(i32x4, ca) : __builtin_bit_cast(i32x4, cb);
+          i32x4 rcv;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            rcv[q] = __builtin_amdgcn_update_dpp(snd[q], snd[q], 0xB1, 0xf, 0xf, false);
+          const f16x8 got = __builtin_bit_cast(f16x8, rcv);
+          const f16x8 first = odd ? got : ca;   // row R, columns (odd ? 32 : 0) + 8 lk
+          const f16x8 second = odd ? cb : got;  // row R + 1, the same columns
+          const int col = cs + (odd ? 32 : 0) + 8 * lk;
+          if (row_a < rows) *(f16x8*)(Ch + (int64_t)row_a * p.ldc + col) = first;
+          if (row_b < rows) *(f16x8*)(Ch + (int64_t)row_b * p.ldc + col) = second;
         }
-        if (lane < 16)
-          p.c_scale[(int64_t)(row_start + row) * p.ldcs + n_tile * (kBN / kScaleCols) + wn] = inv;
       }
+      if (lane < 16 && row < rows && c0 < ncols)
+        p.c_scale[(int64_t)(row_start + row) * p.ldcs + n_tile * (kBN / kScaleCols) + wn] = inv;
     }
   } else if constexpr (EPI == EPI_STORE) {
     // fp32, times row_scale[row] in the RS variant (its vector load is waited for at once,
