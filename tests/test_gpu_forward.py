@@ -34,7 +34,8 @@ CASES = {
     "ds_sigmoid_E16": ("ds_sigmoid", {"E": 16}, 333),
     "skew_E64": ("skew", {"E": 64, "hot_stride": 8}, 500),
     "skew_conc_E64": ("skew_conc", {"E": 64, "hot_stride": 8}, 300),
-    # wide gated shared expert: its dense GEMMs take the large-tile path
+    # wide gated shared expert: its dense GEMMs fill the chip and run on the matrix-core GEMM
+    # (dense tiles; the down GEMM writes fp32 rows, row-scaled by the gate with the atomic combine)
     "shared_wide": ("tiny", {"D": 256, "E": 4, "K": 2, "F": 256, "F_shared": 2048,
                              "shared_gated": True, "dtype": "bf16"}, 2048),
     # degenerate routings: every expert selected (dense mixture), a single expert
