@@ -66,6 +66,25 @@ enum {
                                   top-k sum of "Qwen3.8-Flash-Next 架构笔记 · 04" §2)       */
 };
 
+/* Kernel used for the routed (grouped) expert GEMMs.  AUTO: the matrix-core GEMM with
+ * 256 x 256 tiles for bf16 layers whose operands fit its 32-bit offsets, else the tile GEMM
+ * (256-row tiles when experts average more than 48 rows, 32-row tiles otherwise). */
+typedef enum {
+  MOE_GEMM_AUTO = 0,
+  MOE_GEMM_TILE_32 = 1,   /* tile GEMM, 32 x 128 output tiles (any dtype)                     */
+  MOE_GEMM_TILE_256 = 2,  /* tile GEMM, 256 x 128 output tiles (any dtype)                    */
+  MOE_GEMM_MFMA_256 = 3   /* matrix-core GEMM, 256 x 256 tiles (bf16 layers only; otherwise
+                             MOE_ERR_UNSUPPORTED)                                         */
+} moe_gemm_kernel;
+
+/* Dispatch implementation.  AUTO: one work-group for up to 8192 assignments and E <= 768,
+ * else a histogram launch followed by a scan + scatter launch. */
+typedef enum {
+  MOE_DISPATCH_AUTO = 0,
+  MOE_DISPATCH_ONE_WORKGROUP = 1, /* any T*K; E <= 768 (otherwise MOE_ERR_UNSUPPORTED)        */
+  MOE_DISPATCH_MULTI = 2          /* count, then scan + scatter                               */
+} moe_dispatch_kernel;
+
 /* Problem statement (host struct, read during the call, not retained).
  * v1 limits: D, F and F_shared multiples of 64; 1 <= E <= 1024; 1 <= K <= min(E, 64);
  * T*K < 2^31. */
@@ -89,6 +108,12 @@ typedef struct {
                            others are dropped (inv_perm = -1, excluded from counts) and add
                            nothing to the output                                           */
   int32_t min_capacity; /* floor of C when capacity_factor > 0 (>= 0)                      */
+  int32_t gemm_kernel;  /* moe_gemm_kernel: which GEMM runs the routed experts; 0 (AUTO) =
+                           the library's choice.  A forced choice computes the same result
+                           (within the layer's tolerance) with another tiling, for tests and
+                           tuning; it is never read from the environment               */
+  int32_t dispatch_kernel; /* moe_dispatch_kernel; 0 (AUTO) = the library's choice; forced
+                              choices give bit-identical dispatch results              */
 } moe_problem;
 
 /* Weights, all in `dtype` except logit_bias (fp32).  Layouts follow the fused projections of
@@ -122,6 +147,11 @@ typedef struct {
   int32_t *inv_perm;       /* [T*K] inv_perm[a] = pos, or -1 for a skipped sentinel or an
                               assignment dropped for capacity                              */
   float *shared_gate;      /* [T]   g_t = sigmoid(w_s . x_t)                               */
+  float *select_keys;      /* [T, E] fp32: the value top-K compared for each expert -- the
+                              logit r_te, or with a select_bias the fp32 score + bias
+                              (NaN ranks as -inf, -0 as +0).  Output of moe_route,
+                              moe_route_logits and moe_forward when non-NULL; with the
+                              exported keys, a selection can be checked bit for bit          */
 } moe_routing;
 
 /* Host only.  Bytes of device workspace every entry point below accepts for problem `p`

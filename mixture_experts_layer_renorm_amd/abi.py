@@ -29,11 +29,22 @@ MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1
 MOE_FLAG_ATOMIC_COMBINE = 1
 MOE_FLAG_NO_RENORM = 2
+MOE_GEMM_AUTO = 0
+MOE_GEMM_TILE_32 = 1
+MOE_GEMM_TILE_256 = 2
+MOE_GEMM_MFMA_256 = 3
+MOE_DISPATCH_AUTO = 0
+MOE_DISPATCH_ONE_WORKGROUP = 1
+MOE_DISPATCH_MULTI = 2
+GEMM_KERNELS = {"auto": MOE_GEMM_AUTO, "tile32": MOE_GEMM_TILE_32, "tile256": MOE_GEMM_TILE_256,
+                "mfma": MOE_GEMM_MFMA_256}
+DISPATCH_KERNELS = {"auto": MOE_DISPATCH_AUTO, "one_workgroup": MOE_DISPATCH_ONE_WORKGROUP,
+                    "multi": MOE_DISPATCH_MULTI}
 
 SYMBOLS = ("moe_workspace_size", "moe_route", "moe_route_logits", "moe_dispatch",
            "moe_experts", "moe_combine", "moe_forward", "moe_forward_timed",
            "moe_status_string", "moe_last_error", "moe_describe_plan", "moe_update_select_bias",
-           "moe_router_stats")
+           "moe_router_stats", "moe_peak_hbm_read", "moe_peak_mfma_bf16")
 MOE_STAGE_NAMES = ("router", "topk", "dispatch", "gate_up", "shared", "down", "final")
 MOE_STAGE_COUNT = len(MOE_STAGE_NAMES)
 MOE_STAGE_GATE_UP = MOE_STAGE_NAMES.index("gate_up")
@@ -48,14 +59,15 @@ class moe_problem(ctypes.Structure):
                 ("shared_gated", ctypes.c_int32), ("scoring", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("flags", ctypes.c_uint32), ("capacity_factor", ctypes.c_float),
-                ("min_capacity", ctypes.c_int32)]
+                ("min_capacity", ctypes.c_int32), ("gemm_kernel", ctypes.c_int32),
+                ("dispatch_kernel", ctypes.c_int32)]
 
 
 _WEIGHT_FIELDS = ("w_router", "logit_bias", "w_gate_up", "w_down", "ws_gate_up", "ws_down",
                   "ws_gate", "select_bias")
 _FP32_WEIGHTS = ("logit_bias", "select_bias")
 _ROUTING_FIELDS = ("logits", "topk_idx", "topk_w", "expert_counts", "expert_offsets", "perm",
-                   "inv_perm", "shared_gate")
+                   "inv_perm", "shared_gate", "select_keys")
 
 
 class moe_weights(ctypes.Structure):
@@ -107,6 +119,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_describe_plan.argtypes = [prob]
     lib.moe_describe_plan.restype = ctypes.c_char_p
+    lib.moe_peak_hbm_read.argtypes = [vp, sz, vp, vp]
+    lib.moe_peak_hbm_read.restype = ctypes.c_int
+    lib.moe_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.moe_peak_mfma_bf16.restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -123,7 +139,8 @@ def make_problem(T: int, D: int, E: int, K: int, F: int, F_shared: int = 0,
                  shared_gated: bool = False, scoring: str = "softmax", dtype=torch.bfloat16,
                  out_dtype=None, atomic_combine: bool = False,
                  renormalize: bool = True, capacity_factor: float = 0.0,
-                 min_capacity: int = 0) -> moe_problem:
+                 min_capacity: int = 0, gemm_kernel: str = "auto",
+                 dispatch_kernel: str = "auto") -> moe_problem:
     if scoring not in ("softmax", "sigmoid"):
         raise ValueError(f"scoring must be 'softmax' or 'sigmoid', got {scoring!r}")
     out_dtype = dtype if out_dtype is None else out_dtype
@@ -133,7 +150,9 @@ def make_problem(T: int, D: int, E: int, K: int, F: int, F_shared: int = 0,
                        shared_gated=1 if shared_gated else 0,
                        scoring=MOE_SCORE_SOFTMAX if scoring == "softmax" else MOE_SCORE_SIGMOID,
                        dtype=_DTYPE_CODE[dtype], out_dtype=_DTYPE_CODE[out_dtype], flags=flags,
-                       capacity_factor=capacity_factor, min_capacity=min_capacity)
+                       capacity_factor=capacity_factor, min_capacity=min_capacity,
+                       gemm_kernel=GEMM_KERNELS[gemm_kernel],
+                       dispatch_kernel=DISPATCH_KERNELS[dispatch_kernel])
 
 
 def problem_dtype(p: moe_problem) -> torch.dtype:
@@ -165,7 +184,8 @@ def _weights(p: moe_problem, w: Dict[str, Optional[torch.Tensor]]) -> moe_weight
 
 _ROUTING_DTYPES = {"logits": torch.float32, "topk_idx": torch.int32, "topk_w": torch.float32,
                    "expert_counts": torch.int32, "expert_offsets": torch.int32,
-                   "perm": torch.int32, "inv_perm": torch.int32, "shared_gate": torch.float32}
+                   "perm": torch.int32, "inv_perm": torch.int32, "shared_gate": torch.float32,
+                   "select_keys": torch.float32}
 
 
 def _routing(r: Optional[Dict[str, Optional[torch.Tensor]]]) -> Optional[moe_routing]:
@@ -310,13 +330,35 @@ def moe_forward_timed(p: moe_problem, x: torch.Tensor, weights: Dict, routing: O
                                  _stream(stream), ev))
 
 
+def moe_peak_hbm_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Stream-read all of `buf` (a multiple of 64 KiB) once; sink: >= 2048 fp32."""
+    lib = load_library()
+    if sink.numel() < 2048:
+        raise ValueError("sink must hold 2048 floats")
+    st = lib.moe_peak_hbm_read(_ptr(buf, "buf"), buf.numel() * buf.element_size(),
+                               _ptr(sink, "sink", torch.float32), _stream(stream))
+    if st != MOE_OK:
+        raise MoEError(st, lib.moe_status_string(st).decode())
+
+
+def moe_peak_mfma_bf16(waves: int, iters: int, sink: torch.Tensor, stream=None) -> None:
+    """waves * iters * 8 bf16 MFMAs of 16x16x32 on registers; sink: >= waves fp32."""
+    lib = load_library()
+    if sink.numel() < waves:
+        raise ValueError("sink must hold one float per wave")
+    st = lib.moe_peak_mfma_bf16(waves, iters, _ptr(sink, "sink", torch.float32), _stream(stream))
+    if st != MOE_OK:
+        raise MoEError(st, lib.moe_status_string(st).decode())
+
+
 # ------------------------------------------------------------- allocation helpers ----
 
 def alloc_workspace(p: moe_problem, device="cuda") -> torch.Tensor:
     return torch.empty(max(moe_workspace_size(p), 16), dtype=torch.uint8, device=device)
 
 
-def alloc_routing(p: moe_problem, device="cuda", logits: bool = True) -> Dict[str, torch.Tensor]:
+def alloc_routing(p: moe_problem, device="cuda", logits: bool = True,
+                  select_keys: bool = False) -> Dict[str, torch.Tensor]:
     T, E, K = p.T, p.E, p.K
     i32, f32 = torch.int32, torch.float32
     r = {"topk_idx": torch.empty((T, K), dtype=i32, device=device),
@@ -328,4 +370,6 @@ def alloc_routing(p: moe_problem, device="cuda", logits: bool = True) -> Dict[st
          "shared_gate": torch.empty(max(T, 1), dtype=f32, device=device)}
     if logits:
         r["logits"] = torch.empty((T, E), dtype=f32, device=device)
+    if select_keys:
+        r["select_keys"] = torch.empty((T, E), dtype=f32, device=device)
     return r

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["gemm.hip", "gemm_stream.hip", "gemm_mfma.hip", "route.hip", "dispatch.hip", "combine.hip",
+SOURCES = ["gemm.hip", "gemm_mfma.hip", "peaks.hip", "route.hip", "dispatch.hip", "combine.hip",
            "stats.hip", "api.cpp"]
 
 COMMON = [

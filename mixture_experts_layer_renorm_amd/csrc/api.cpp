@@ -41,6 +41,26 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t esize(int dtype) { return dtype == MOE_DTYPE_BF16 ? 2 : 4; }
 
+// The matrix-core GEMM addresses its operands with 32-bit byte offsets from a uniform base:
+// the grouped GEMMs' token rows ([T*K, max(D, F)] at most, via x_perm or H) and one expert's
+// weights must each span less than 4 GiB.
+bool mfma_fits(const moe_problem* p) {
+  const int64_t es = (int64_t)esize(p->dtype);
+  const int64_t wide = p->D > p->F ? p->D : p->F;
+  const int64_t lim = (int64_t)1 << 32;
+  return p->dtype == MOE_DTYPE_BF16 && p->T * p->K * wide * es < lim &&
+         (int64_t)2 * p->F * p->D * es < lim;
+}
+
+// The same limit for the shared expert's dense GEMMs: x [T, D], Hs [T, F_s] and the shared
+// weights ([2 F_s, D], [D, F_s]).
+bool mfma_fits_shared(const moe_problem* p) {
+  const int64_t es = (int64_t)esize(p->dtype);
+  const int64_t lim = (int64_t)1 << 32;
+  return p->dtype == MOE_DTYPE_BF16 && p->T * p->D * es < lim && p->T * p->F_shared * es < lim &&
+         (int64_t)2 * p->F_shared * p->D * es < lim;
+}
+
 int check_problem(const moe_problem* p) {
   if (!p) return fail(MOE_ERR_INVALID_ARG, "problem is NULL");
   if (p->T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
@@ -68,6 +88,17 @@ int check_problem(const moe_problem* p) {
   if (p->K > 64) return fail(MOE_ERR_UNSUPPORTED, "K > 64");
   if (p->T * (int64_t)p->K >= (int64_t)1 << 31) return fail(MOE_ERR_UNSUPPORTED, "T*K >= 2^31");
   if (p->T * (int64_t)p->D >= (int64_t)1 << 40) return fail(MOE_ERR_UNSUPPORTED, "T*D too large");
+  if (p->gemm_kernel < MOE_GEMM_AUTO || p->gemm_kernel > MOE_GEMM_MFMA_256)
+    return fail(MOE_ERR_INVALID_ARG, "unknown gemm_kernel %d", p->gemm_kernel);
+  if (p->dispatch_kernel < MOE_DISPATCH_AUTO || p->dispatch_kernel > MOE_DISPATCH_MULTI)
+    return fail(MOE_ERR_INVALID_ARG, "unknown dispatch_kernel %d", p->dispatch_kernel);
+  if (p->gemm_kernel == MOE_GEMM_MFMA_256 && !mfma_fits(p))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "gemm_kernel MFMA_256 needs a bf16 layer whose token rows and expert weights "
+                "each span less than 4 GiB");
+  if (!moe::dispatch_supported(p->E, p->dispatch_kernel))
+    return fail(MOE_ERR_UNSUPPORTED, "dispatch_kernel ONE_WORKGROUP needs E <= %d",
+                moe::kDispatchOneWgMaxE);
   return MOE_OK;
 }
 
@@ -83,56 +114,22 @@ int32_t capacity(const moe_problem* p) {
 }
 bool gated(const moe_problem* p) { return p->F_shared > 0 && p->shared_gated; }
 
-// Grouped (routed-expert) GEMMs.  bf16 layers run every expert group on the matrix-core GEMM
-// (256 x 256 tiles, a partial tile computed in 32-row steps), one tile map of up to 256-row M
-// tiles.  fp32 layers (and operands of 4 GiB or more) use the tile GEMM with one map.
-// MOE_GROUPED_TILE overrides the plan for tuning and for the tests that cover every kernel at
-// small sizes: small, large, stream64, stream128, stream192 and mfma force one map with the
-// named tile; split192 puts experts with up to 192 rows on the weight-streaming GEMM and the
-// larger ones on the matrix-core GEMM, in two maps that the dispatch kernel fills on the
-// device (the host does not see the per-expert counts).  The streaming and MFMA shapes apply
-// to bf16 only.  The streaming and matrix-core GEMMs address their operands with 32-bit
-// offsets from a uniform base: token rows ([T*K, max(D, F)] at most, via x_perm or H) and one
-// expert's weights must each span less than 4 GiB.
-bool stream_fits(const moe_problem* p) {
-  const int64_t es = (int64_t)esize(p->dtype);
-  const int64_t wide = p->D > p->F ? p->D : p->F;
-  const int64_t lim = (int64_t)1 << 32;
-  return p->T * p->K * wide * es < lim && (int64_t)2 * p->F * p->D * es < lim;
-}
-
-struct GroupedPlan {
-  moe::TileCfg cfg0, cfg1;
-  int split;  // < 0: one map
-};
-
-GroupedPlan grouped_plan(const moe_problem* p) {
-  const bool bf = p->dtype == MOE_DTYPE_BF16 && stream_fits(p);
-  if (const char* o = std::getenv("MOE_GROUPED_TILE")) {
-    if (!std::strcmp(o, "small")) return {moe::TILE_SMALL, moe::TILE_SMALL, -1};
-    if (!std::strcmp(o, "large")) return {moe::TILE_LARGE, moe::TILE_LARGE, -1};
-    if (bf && !std::strcmp(o, "stream64")) return {moe::TILE_STREAM_64, moe::TILE_STREAM_64, -1};
-    if (bf && !std::strcmp(o, "stream128"))
-      return {moe::TILE_STREAM_128, moe::TILE_STREAM_128, -1};
-    if (bf && !std::strcmp(o, "stream192"))
-      return {moe::TILE_STREAM_192, moe::TILE_STREAM_192, -1};
-    if (bf && !std::strcmp(o, "mfma")) return {moe::TILE_MFMA, moe::TILE_MFMA, -1};
-    if (bf && !std::strcmp(o, "split192"))  // streaming GEMM up to 192 rows, matrix-core above
-      return {moe::TILE_STREAM_192, moe::TILE_MFMA, 192};
+// Grouped (routed-expert) GEMMs, one tile map of M tiles of up to tile_bm rows.  bf16 layers
+// run every expert group on the matrix-core GEMM (256 x 256 tiles, a partial tile computed in
+// 32-row steps): at decode sizes its direct-to-LDS weight ring streams the weights at the
+// speed of its load pattern, and groups of hundreds of rows keep the matrix cores busy.  fp32
+// layers and operands past the 32-bit offsets use the tile GEMM.  moe_problem.gemm_kernel
+// forces one of them (tests and tuning).
+moe::TileCfg grouped_cfg(const moe_problem* p) {
+  switch (p->gemm_kernel) {
+    case MOE_GEMM_TILE_32: return moe::TILE_SMALL;
+    case MOE_GEMM_TILE_256: return moe::TILE_LARGE;
+    case MOE_GEMM_MFMA_256: return moe::TILE_MFMA;  // check_problem: bf16, fits
+    default: break;
   }
-  // bf16: the matrix-core GEMM for every group size.  Its direct-to-LDS weight ring streams
-  // the weights faster than the register ring of the streaming GEMM (5.7 vs 5.5 TB/s on the
-  // gate_up of a 64-token batch), and a group's partly filled tile costs only its 32-row
-  // blocks, where the streaming GEMM runs all of its 192 rows (a 4096-token 35B-A3B-shaped
-  // layer: gate_up 221 vs 231 us; a 8192-token 397B-A17B-shaped one: 1706 vs 1882 us).
-  if (bf) return {moe::TILE_MFMA, moe::TILE_MFMA, -1};
+  if (mfma_fits(p)) return moe::TILE_MFMA;
   const double mean = (double)(p->T * p->K) / p->E;
-  const moe::TileCfg c = mean <= 48 ? moe::TILE_SMALL : moe::TILE_LARGE;
-  return {c, c, -1};
-}
-
-moe::TileSplit tile_split(const GroupedPlan& g, int64_t max_mtiles) {
-  return {moe::tile_bm(g.cfg0), moe::tile_bm(g.cfg1), g.split, max_mtiles};
+  return mean <= 48 ? moe::TILE_SMALL : moe::TILE_LARGE;
 }
 
 // Router: bf16 batches of up to 1024 tokens use the split-K matrix-core router (partial sums
@@ -143,13 +140,20 @@ int router_ks(const moe_problem* p) {
   return router_split(p) ? moe::router_kslices(p->T, p->D, p->E, gated(p) ? 1 : 0) : 1;
 }
 
-// Dense GEMMs: large tiles unless they would leave CUs idle.  The fp32 router (extra gate column,
-// column bias) stays on the tile GEMM; the shared expert's bf16 GEMMs take the MFMA GEMM.
-moe::TileCfg dense_cfg(int64_t M, int64_t N, int dtype = MOE_DTYPE_F32) {
+// Dense GEMMs: large tiles unless they would leave CUs idle.  The router (extra gate column,
+// column bias) stays on the tile GEMM.
+moe::TileCfg dense_cfg(int64_t M, int64_t N) {
   const int64_t bm = moe::tile_bm(moe::TILE_LARGE), bn = moe::tile_bn(moe::TILE_LARGE);
   const bool big = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) >= moe::kCus;
-  if (!big) return moe::TILE_SMALL;
-  return dtype == MOE_DTYPE_BF16 ? moe::TILE_MFMA : moe::TILE_LARGE;
+  return big ? moe::TILE_LARGE : moe::TILE_SMALL;
+}
+
+// The shared expert's two GEMMs: the matrix-core GEMM (dense 256 x 256 tiles) for bf16
+// layers when they fill the chip and every operand fits its 32-bit offsets; the 64-bit tile
+// GEMM otherwise.
+moe::TileCfg shared_cfg(const moe_problem* p) {
+  const moe::TileCfg c = dense_cfg(p->T, (int64_t)2 * p->F_shared);
+  return c == moe::TILE_LARGE && mfma_fits_shared(p) ? moe::TILE_MFMA : c;
 }
 
 // Workspace layout: every region 256-byte aligned.
@@ -186,7 +190,7 @@ Layout layout(const moe_problem* p) {
   L.perm = take((size_t)A * 4);
   L.inv_perm = take((size_t)A * 4);
   L.seg_counts = take((size_t)moe::dispatch_num_segments(A) * E * 4);
-  L.tiles = take((size_t)2 * L.max_mtiles * moe::kTileStride * 4);  // two maps
+  L.tiles = take((size_t)L.max_mtiles * moe::kTileStride * 4);
   L.tile_count = take(16);
   L.H = take((size_t)A * p->F * es);
   L.Hs = take((size_t)T * p->F_shared * es);
@@ -279,24 +283,19 @@ hipError_t run_router(const moe_problem* p, const void* x, const moe_weights* w,
   return moe::launch_gemm(p->dtype, cfg, moe::EPI_STORE, g, (p->T + bm - 1) / bm, s);
 }
 
-// gate_up over the tile map: rows gathered from x through perm (or read from x_perm).
-// Launches a grouped GEMM over map 0 and, if the plan splits, map 1.
-hipError_t launch_grouped(const moe_problem* p, const GroupedPlan& plan, moe::Epilogue epi,
+// A grouped GEMM over the tile map.
+hipError_t launch_grouped(const moe_problem* p, moe::TileCfg cfg, moe::Epilogue epi,
                           moe::GemmParams g, const int32_t* tiles, const int32_t* tile_count,
                           int64_t max_mtiles, hipStream_t s) {
   g.tiles = tiles;
   g.tile_count = tile_count;
   g.rows_bound = (int32_t)p->T;  // an expert receives at most one row per token
-  hipError_t e = moe::launch_gemm(p->dtype, plan.cfg0, epi, g, max_mtiles, s);
-  if (e != hipSuccess || plan.split < 0) return e;
-  g.tiles = tiles + max_mtiles * moe::kTileStride;
-  g.tile_count = tile_count + 1;
-  return moe::launch_gemm(p->dtype, plan.cfg1, epi, g, max_mtiles, s);
+  return moe::launch_gemm(p->dtype, cfg, epi, g, max_mtiles, s);
 }
 
 hipError_t run_gate_up(const moe_problem* p, const void* x, const void* x_perm, const void* w_gu,
                        const int32_t* perm, const int32_t* tiles, const int32_t* tile_count,
-                       int64_t max_mtiles, void* H, const GroupedPlan& plan, hipStream_t s) {
+                       int64_t max_mtiles, void* H, moe::TileCfg plan, hipStream_t s) {
   const size_t es = esize(p->dtype);
   moe::GemmParams g{};
   g.A = (const char*)(x_perm ? x_perm : x);
@@ -314,7 +313,7 @@ hipError_t run_gate_up(const moe_problem* p, const void* x, const void* x_perm, 
 }
 
 hipError_t run_down(const moe_problem* p, const void* H, const void* w_d, const int32_t* tiles,
-                    const int32_t* tile_count, int64_t max_mtiles, const GroupedPlan& plan,
+                    const int32_t* tile_count, int64_t max_mtiles, moe::TileCfg plan,
                     void* y_perm, float* acc, const int32_t* perm, const float* topk_w,
                     hipStream_t s, float* y_scale = nullptr) {
   const size_t es = esize(p->dtype);
@@ -342,24 +341,20 @@ hipError_t run_down(const moe_problem* p, const void* H, const void* w_d, const 
 }
 
 // Whether moe_forward keeps the routed expert rows (y_perm) as fp16 with a power-of-two factor
-// per row and 256-column block instead of fp32: for bf16 layers whose grouped GEMMs are the
-// streaming / matrix-core kernels (the only ones with that epilogue).  Half the bytes of the
-// down GEMM's stores and of the combine's reads; the factor keeps every value below 2^15, so
-// nothing overflows, and the 11-bit significand adds about 2^-12 of a block's largest value,
-// far below the bf16 rounding of H.
-bool compact_rows(const moe_problem* p, const GroupedPlan& plan) {
-  auto ok = [](moe::TileCfg c) {
-    return c == moe::TILE_STREAM_64 || c == moe::TILE_STREAM_128 || c == moe::TILE_STREAM_192 ||
-           c == moe::TILE_MFMA;
-  };
-  return p->dtype == MOE_DTYPE_BF16 && ok(plan.cfg0) && (plan.split < 0 || ok(plan.cfg1));
+// per row and 128-column block instead of fp32: for bf16 layers whose grouped GEMM is the
+// matrix-core kernel (the only one with that epilogue).  Half the bytes of the down GEMM's
+// stores and of the combine's reads; the factor keeps every value below 2^15, so nothing
+// overflows, and the 11-bit significand adds about 2^-12 of a block's largest value, far
+// below the bf16 rounding of H.
+bool compact_rows(const moe_problem* p, moe::TileCfg plan) {
+  return p->dtype == MOE_DTYPE_BF16 && plan == moe::TILE_MFMA;
 }
 
 // Shared expert on all T tokens: Hs = SwiGLU gate/up of x; out = row_scale * (Hs Ws_downᵀ).
 hipError_t run_shared(const moe_problem* p, const void* x, const moe_weights* w, void* Hs,
                       float* out, const float* row_scale, hipStream_t s) {
   const size_t es = esize(p->dtype);
-  const moe::TileCfg cfg = dense_cfg(p->T, (int64_t)2 * p->F_shared, p->dtype);
+  const moe::TileCfg cfg = shared_cfg(p);
   const int bm = moe::tile_bm(cfg);
   const int64_t mt = (p->T + bm - 1) / bm;
   moe::GemmParams g{};
@@ -430,9 +425,7 @@ const char* moe_describe_plan(const moe_problem* p) {
   g_last_error.clear();
   if (check_problem(p)) return text.c_str();
   auto name = [](moe::TileCfg c) -> std::string {
-    const bool stream = c == moe::TILE_STREAM_64 || c == moe::TILE_STREAM_128 ||
-                        c == moe::TILE_STREAM_192;
-    const char* kind = stream ? "stream " : c == moe::TILE_MFMA ? "mfma " : "tile ";
+    const char* kind = c == moe::TILE_MFMA ? "mfma " : "tile ";
     return std::string(kind) + std::to_string(moe::tile_bm(c)) + "x" +
            std::to_string(moe::tile_bn(c));
   };
@@ -441,16 +434,13 @@ const char* moe_describe_plan(const moe_problem* p) {
           ? "split-K mfma 16x64, " + std::to_string(router_ks(p)) + " K slice(s)"
           : name(dense_cfg(p->T, p->E + (gated(p) ? 1 : 0)));
   text = "router: " + router + "; dispatch: " +
-         (moe::dispatch_fused(p->T * p->K, p->E) ? "one work-group" : "count, then scan+scatter") +
-         "; grouped gate_up/down: " + name(grouped_plan(p).cfg0);
-  if (grouped_plan(p).split >= 0)
-    text += " (experts with <= " + std::to_string(grouped_plan(p).split) + " rows), " +
-            name(grouped_plan(p).cfg1) + " (larger)";
-  if (has_shared(p))
-    text += "; shared: " + name(dense_cfg(p->T, (int64_t)2 * p->F_shared, p->dtype));
+         (moe::dispatch_fused(p->T * p->K, p->E, p->dispatch_kernel) ? "one work-group"
+                                                                      : "count, then scan+scatter") +
+         "; grouped gate_up/down: " + name(grouped_cfg(p));
+  if (has_shared(p)) text += "; shared: " + name(shared_cfg(p));
   text += (p->flags & MOE_FLAG_ATOMIC_COMBINE)
               ? "; combine: fp32 atomics in the down epilogue"
-              : compact_rows(p, grouped_plan(p))
+              : compact_rows(p, grouped_cfg(p))
                     ? "; combine: gather in slot order over fp16 rows with block factors"
                     : "; combine: gather in slot order";
   return text.c_str();
@@ -478,6 +468,7 @@ int moe_route(const moe_problem* p, const void* x, const moe_weights* w, moe_rou
   MOE_CHECK_PTR(r->topk_w, "topk_w");
   MOE_CHECK_OPT(r->logits, "logits");
   MOE_CHECK_OPT(r->shared_gate, "shared_gate");
+  MOE_CHECK_OPT(r->select_keys, "select_keys");
   Layout L;
   if ((st = check_ws(p, workspace, workspace_bytes, &L))) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -489,6 +480,7 @@ int moe_route(const moe_problem* p, const void* x, const moe_weights* w, moe_rou
   ta.idx = r->topk_idx;
   ta.w = r->topk_w;
   ta.logits_out = r->logits;
+  ta.keys_out = r->select_keys;
   ta.gate_out = want_gate ? r->shared_gate : nullptr;
   ta.sel_bias = w->select_bias;
   MOE_HIP_TRY(moe::launch_topk(ta, s), "top-K launch");
@@ -506,8 +498,10 @@ int moe_route_logits(const moe_problem* p, const float* logits, const float* sel
   if (!r) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
   MOE_CHECK_PTR(r->topk_idx, "topk_idx");
   MOE_CHECK_PTR(r->topk_w, "topk_w");
+  MOE_CHECK_OPT(r->select_keys, "select_keys");
   moe::TopkArgs ta{};
   ta.src = logits;
+  ta.keys_out = r->select_keys;
   ta.ks = 1;
   ta.ld = p->E;
   ta.T = p->T;
@@ -574,8 +568,7 @@ int moe_dispatch(const moe_problem* p, const void* x, moe_routing* r, void* x_pe
   const int64_t A = p->T * p->K;
   MOE_HIP_TRY(moe::launch_dispatch(r->topk_idx, A, p->E, at<int32_t>(workspace, L.seg_counts),
                                    r->expert_counts, r->expert_offsets, r->perm, r->inv_perm,
-                                   capacity(p), moe::TileSplit{32, 32, -1, 0}, nullptr, nullptr,
-                                   s),
+                                   capacity(p), p->dispatch_kernel, 0, nullptr, nullptr, s),
               "dispatch launch");
   if (x_perm)
     MOE_HIP_TRY(moe::launch_gather_rows(x, p->D, (int)esize(p->dtype), r->perm, r->expert_offsets,
@@ -604,11 +597,11 @@ int moe_experts(const moe_problem* p, const void* x, const void* x_perm, const m
   Layout L;
   if ((st = check_ws(p, workspace, workspace_bytes, &L))) return st;
   hipStream_t s = (hipStream_t)stream;
-  const GroupedPlan plan = grouped_plan(p);
+  const moe::TileCfg plan = grouped_cfg(p);
   int32_t* tiles = at<int32_t>(workspace, L.tiles);
   int32_t* tile_count = at<int32_t>(workspace, L.tile_count);
-  MOE_HIP_TRY(moe::launch_tile_map(r->expert_offsets, p->E, tile_split(plan, L.max_mtiles), tiles,
-                                   tile_count, s),
+  MOE_HIP_TRY(moe::launch_tile_map(r->expert_offsets, p->E, moe::tile_bm(plan), tiles, tile_count,
+                                   s),
               "tile map launch");
   void* H = at<void>(workspace, L.H);
   MOE_HIP_TRY(run_gate_up(p, x, x_perm, w->w_gate_up, r->perm, tiles, tile_count, L.max_mtiles, H,
@@ -672,6 +665,7 @@ int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_
     MOE_CHECK_OPT(r.perm, "perm");
     MOE_CHECK_OPT(r.inv_perm, "inv_perm");
     MOE_CHECK_OPT(r.shared_gate, "shared_gate");
+    MOE_CHECK_OPT(r.select_keys, "select_keys");
   }
   Layout L;
   if ((st = check_ws(p, workspace, workspace_bytes, &L))) return st;
@@ -701,17 +695,18 @@ int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_
   ta.idx = r.topk_idx;
   ta.w = r.topk_w;
   ta.logits_out = r.logits;  // only if the caller asked for them
+  ta.keys_out = r.select_keys;
   ta.gate_out = g ? r.shared_gate : nullptr;
   ta.sel_bias = w->select_bias;
   MOE_HIP_TRY(moe::launch_topk(ta, s), "top-K launch");
   // 2. dispatch + tile map
-  const GroupedPlan plan = grouped_plan(p);
+  const moe::TileCfg plan = grouped_cfg(p);
   int32_t* tiles = at<int32_t>(ws, L.tiles);
   int32_t* tile_count = at<int32_t>(ws, L.tile_count);
   MOE_HIP_TRY(mark(MOE_STAGE_DISPATCH), "event record");
   MOE_HIP_TRY(moe::launch_dispatch(r.topk_idx, A, p->E, at<int32_t>(ws, L.seg_counts),
                                    r.expert_counts, r.expert_offsets, r.perm, r.inv_perm,
-                                   capacity(p), tile_split(plan, L.max_mtiles), tiles,
+                                   capacity(p), p->dispatch_kernel, moe::tile_bm(plan), tiles,
                                    tile_count, s),
               "dispatch launch");
   // 3. routed gate_up with SiLU*up

@@ -18,9 +18,6 @@
 // Expert capacity ("1.6 混合专家（MoE）" §三): with a cap C, scan counts min(t_e, C) rows per
 // expert (so offsets and tile maps cover only kept rows) and scatter drops every assignment
 // whose rank q is C or more (inv_perm = -1): each expert keeps its first C assignments.
-#include <cstdlib>
-#include <cstring>
-
 #include "kernels.h"
 
 namespace moe {
@@ -31,7 +28,7 @@ constexpr int kSegRounds = 8;                // 64-id rounds per segment
 constexpr int kSegLen = 64 * kSegRounds;      // assignments per segment (one wave)
 // Single-work-group dispatch up to this many assignments (its LDS holds 18 ints per expert).
 constexpr int64_t kFusedMaxA = 8192;
-constexpr int kFusedMaxE = 768;
+constexpr int kFusedMaxE = kDispatchOneWgMaxE;
 
 __device__ __forceinline__ int wave_prefix_exclusive(int v, int lane) {
   int x = v;
@@ -93,52 +90,41 @@ __global__ void __launch_bounds__(256) count_kernel(const int32_t* __restrict__ 
   for (int e = lane; e < E; e += 64) seg_counts[seg * E + e] = hist[e];
 }
 
-// Builds the tile maps from per-expert counts held in LDS.  One entry per M tile:
-// {expert, first row position, rows, 0, first M tile of the expert, M tiles of the expert};
-// experts with more than ts.split rows go to map 1 (bm1-row tiles), the others to map 0.
-// An expert's rows are split evenly over its ceil(c / bm) M tiles (the first c % mt tiles one
-// row more): its tiles then cost the same, run in step on one XCD and fetch each weight tile
-// once into its L2 for all of them (a full tile and a short last one drift apart, and each
-// streams the weights from memory by itself).
+// Builds the tile map from per-expert counts held in LDS.  One entry per M tile:
+// {expert, first row position, rows, 0, first M tile of the expert, M tiles of the expert, 0,
+// 0}.  An expert's rows are split evenly over its ceil(c / bm) M tiles (the first c % mt tiles
+// one row more): its tiles then cost the same, run in step on one XCD and fetch each weight
+// tile once into its L2 for all of them (a full tile and a short last one drift apart, and
+// each streams the weights from memory by itself).
 template <int NT>
-__device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, const TileSplit ts,
-                            int* scratch, int32_t* tiles, int32_t* tile_count) {
-  int32_t* maps[2] = {tiles, tiles + ts.map1_entries * kTileStride};
-  const int bms[2] = {ts.bm0, ts.bm1};
-  int total[2] = {0, 0};
+__device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, int bm, int* scratch,
+                            int32_t* tiles, int32_t* tile_count) {
+  int total = 0;
   for (int base = 0; base < E; base += NT) {
     const int e = base + threadIdx.x;
     const int c = e < E ? cnt_lds[e] : 0;
-    const int which = (ts.split >= 0 && c > ts.split) ? 1 : 0;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int bm = bms[m];
-      const int mt = which == m ? (c + bm - 1) / bm : 0;
-      int chunk_total;
-      const int first = block_exclusive_scan<NT>(mt, scratch, &chunk_total) + total[m];
-      const int base_rows = mt > 0 ? c / mt : 0, extra = mt > 0 ? c % mt : 0;
-      for (int q = 0; q < mt; ++q) {
-        int32_t* ent = maps[m] + (int64_t)(first + q) * kTileStride;
-        ent[0] = e;
-        ent[1] = off_lds[e] + q * base_rows + min(q, extra);
-        ent[2] = base_rows + (q < extra ? 1 : 0);
-        ent[3] = 0;
-        ent[4] = first;
-        ent[5] = mt;
-        ent[6] = 0;
-        ent[7] = 0;
-      }
-      total[m] += chunk_total;
+    const int mt = (c + bm - 1) / bm;
+    int chunk_total;
+    const int first = block_exclusive_scan<NT>(mt, scratch, &chunk_total) + total;
+    const int base_rows = mt > 0 ? c / mt : 0, extra = mt > 0 ? c % mt : 0;
+    for (int q = 0; q < mt; ++q) {
+      int32_t* ent = tiles + (int64_t)(first + q) * kTileStride;
+      ent[0] = e;
+      ent[1] = off_lds[e] + q * base_rows + min(q, extra);
+      ent[2] = base_rows + (q < extra ? 1 : 0);
+      ent[3] = 0;
+      ent[4] = first;
+      ent[5] = mt;
+      ent[6] = 0;
+      ent[7] = 0;
     }
+    total += chunk_total;
   }
-  if (threadIdx.x == 0) {
-    tile_count[0] = total[0];
-    tile_count[1] = total[1];
-  }
+  if (threadIdx.x == 0) tile_count[0] = total;
 }
 
 __global__ void __launch_bounds__(kScanThreads) tile_map_kernel(const int32_t* __restrict__ offsets,
-                                                                int E, const TileSplit ts,
+                                                                int E, int bm,
                                                                 int32_t* __restrict__ tiles,
                                                                 int32_t* __restrict__ tile_count) {
   extern __shared__ int sm[];
@@ -150,7 +136,7 @@ __global__ void __launch_bounds__(kScanThreads) tile_map_kernel(const int32_t* _
     cnt[e] = offsets[e + 1] - offsets[e];
   }
   __syncthreads();
-  build_tiles<kScanThreads>(cnt, off, E, ts, scratch, tiles, tile_count);
+  build_tiles<kScanThreads>(cnt, off, E, bm, scratch, tiles, tile_count);
 }
 
 // Scan and scatter in one launch.  Work-group b owns segments [8 b, 8 b + 8), one per wave.
@@ -170,7 +156,7 @@ __global__ void __launch_bounds__(kSSThreads) scan_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t A, int E, int nbits, int cap, int64_t nseg,
     const int32_t* __restrict__ seg_counts, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
-    const TileSplit ts, int32_t* __restrict__ tiles, int32_t* __restrict__ tile_count) {
+    const int bm, int32_t* __restrict__ tiles, int32_t* __restrict__ tile_count) {
   extern __shared__ int sm[];
   int* run = sm;                      // [kSSWaves][E]: next rank in each expert, per segment
   int* cnt = run + kSSWaves * E;      // [E] rows kept
@@ -215,7 +201,7 @@ __global__ void __launch_bounds__(kSSThreads) scan_scatter_kernel(
   // the tile maps come from the extra last work-group, which owns no segment, so that no
   // scatter waits for them
   if (tiles && blockIdx.x == gridDim.x - 1) {
-    build_tiles<kSSThreads>(cnt, off, E, ts, scratch, tiles, tile_count);
+    build_tiles<kSSThreads>(cnt, off, E, bm, scratch, tiles, tile_count);
     return;
   }
 
@@ -273,7 +259,7 @@ __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
     const int32_t* __restrict__ idx, int64_t A, int E, int nbits, int cap,
     int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
-    const TileSplit ts, int32_t* __restrict__ tiles, int32_t* __restrict__ tile_count) {
+    const int bm, int32_t* __restrict__ tiles, int32_t* __restrict__ tile_count) {
   extern __shared__ int sm[];
   int* hist = sm;                       // [kFusedWaves][E]: counts, then running ranks
   int* cnt = hist + kFusedWaves * E;    // [E]
@@ -324,7 +310,7 @@ __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
   }
   if (threadIdx.x == 0) offsets[E] = total;
   __syncthreads();
-  if (tiles) build_tiles<kScanThreads>(cnt, off, E, ts, scratch, tiles, tile_count);
+  if (tiles) build_tiles<kScanThreads>(cnt, off, E, bm, scratch, tiles, tile_count);
   __syncthreads();
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t b0 = a_begin; b0 < a_end; b0 += 64 * kFusedBatch) {
@@ -385,28 +371,27 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(const V* __restrict__ 
 
 int dispatch_segment_len(int64_t) { return kSegLen; }
 
-bool dispatch_fused(int64_t A, int E) {
-  bool fused = A <= kFusedMaxA && E <= kFusedMaxE;
-  if (const char* o = std::getenv("MOE_DISPATCH")) {
-    if (!std::strcmp(o, "fused")) fused = E <= kFusedMaxE;
-    if (!std::strcmp(o, "multi")) fused = false;
-  }
-  return fused;
+bool dispatch_supported(int E, int path) { return path != 1 || E <= kFusedMaxE; }
+
+bool dispatch_fused(int64_t A, int E, int path) {
+  if (path == 1) return true;
+  if (path == 2) return false;
+  return A <= kFusedMaxA && E <= kFusedMaxE;
 }
 
 int64_t dispatch_num_segments(int64_t A) { return (A + kSegLen - 1) / kSegLen; }
 
 hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_counts,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                           int cap, const TileSplit& ts, int32_t* tiles, int32_t* tile_count,
+                           int cap, int path, int bm, int32_t* tiles, int32_t* tile_count,
                            hipStream_t stream) {
   const int64_t nseg = dispatch_num_segments(A);
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
-  if (dispatch_fused(A, E)) {
+  if (dispatch_fused(A, E, path)) {
     const size_t lds = (size_t)((kFusedWaves + 2) * E + 32) * sizeof(int);
     hipLaunchKernelGGL(dispatch_fused_kernel, dim3(1), dim3(kScanThreads), lds, stream, idx, A,
-                       E, nbits, cap, counts, offsets, perm, inv_perm, ts, tiles, tile_count);
+                       E, nbits, cap, counts, offsets, perm, inv_perm, bm, tiles, tile_count);
     return hipGetLastError();
   }
   const dim3 g((unsigned)((nseg + 3) / 4)), b(256);
@@ -417,14 +402,14 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_co
   const size_t lds = (size_t)((kSSWaves + 2) * E + 32) * sizeof(int);
   const unsigned groups = (unsigned)((nseg + kSSWaves - 1) / kSSWaves) + (tiles ? 1 : 0);
   hipLaunchKernelGGL(scan_scatter_kernel, dim3(groups), dim3(kSSThreads), lds, stream, idx, A, E, nbits, cap, nseg, seg_counts,
-                     counts, offsets, perm, inv_perm, ts, tiles, tile_count);
+                     counts, offsets, perm, inv_perm, bm, tiles, tile_count);
   return hipGetLastError();
 }
 
-hipError_t launch_tile_map(const int32_t* offsets, int E, const TileSplit& ts, int32_t* tiles,
+hipError_t launch_tile_map(const int32_t* offsets, int E, int bm, int32_t* tiles,
                            int32_t* tile_count, hipStream_t stream) {
   const size_t lds = (size_t)(2 * E + 32) * sizeof(int);
-  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(kScanThreads), lds, stream, offsets, E, ts,
+  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(kScanThreads), lds, stream, offsets, E, bm,
                      tiles, tile_count);
   return hipGetLastError();
 }

@@ -70,17 +70,10 @@ struct GemmParams {
 enum TileCfg : int {
   TILE_SMALL = 0,       // tile GEMM, BM=32,  BN=128
   TILE_LARGE = 1,       // tile GEMM, BM=256, BN=128
-  TILE_STREAM_64 = 2,   // weight-streaming GEMM, BM=64, bf16 only
-  TILE_STREAM_192 = 3,  // weight-streaming GEMM, BM=192, bf16 only
-  TILE_STREAM_128 = 4,  // weight-streaming GEMM, BM=128, bf16 only
-  TILE_MFMA = 5,        // matrix-core GEMM, 256 x 256 tiles, bf16 only, no B2 / col_bias
+  TILE_MFMA = 2,        // matrix-core GEMM, 256 x 256 tiles, bf16 only, no B2 / col_bias
 };
 int tile_bm(TileCfg cfg);
 int tile_bn(TileCfg cfg);
-
-// Grouped weight-streaming GEMM (tile map required, no B2 column), bf16.
-hipError_t launch_stream_gemm(TileCfg cfg, Epilogue epi, const GemmParams& p, int64_t max_mtiles,
-                              hipStream_t stream);
 
 // Matrix-core grouped or dense GEMM (256 x 256 tiles), bf16.
 hipError_t launch_mfma_gemm(Epilogue epi, const GemmParams& p, int64_t max_mtiles,
@@ -92,8 +85,9 @@ hipError_t launch_gemm(int dtype, TileCfg cfg, Epilogue epi, const GemmParams& p
 
 // Router top-K.  The logit of (t, e) is the sum, in slice order, of src[q * slice_stride +
 // t * ld + e] over q < ks (ks = 1: src is the logits matrix).  Writes idx/w [T, K]; optionally
-// the summed logits [T, E] to logits_out, and sigmoid of the gate logit (same summation over
-// gate_src[q * slice_stride + t * gate_ld]) to gate_out [T].
+// the summed logits [T, E] to logits_out, the selection keys [T, E] (the logit, or with
+// sel_bias the fp32 score + bias) to keys_out, and sigmoid of the gate logit (same summation
+// over gate_src[q * slice_stride + t * gate_ld]) to gate_out [T].
 struct TopkArgs {
   const float* src;
   int ks;
@@ -104,6 +98,7 @@ struct TopkArgs {
   int32_t* idx;
   float* w;
   float* logits_out;
+  float* keys_out;
   const float* gate_src;
   int64_t gate_ld;
   float* gate_out;
@@ -120,28 +115,24 @@ hipError_t launch_router_bf16(const void* x, const void* w_router, const void* w
                               const float* bias, int64_t T, int D, int E, int ks, float* part,
                               hipStream_t stream);
 
-// Tiling of the grouped GEMMs.  Experts with at most `split` rows are tiled with bm0-row M
-// tiles into map 0, larger ones with bm1-row tiles into map 1 (written map1_entries entries
-// after map 0); split < 0 puts every expert in map 0.  tile_count[0..1] receive the sizes.
-struct TileSplit {
-  int bm0, bm1, split;
-  int64_t map1_entries;
-};
-
-// Dispatch.
+// Dispatch.  path: 0 = automatic, 1 = one work-group, 2 = count then scan + scatter (the
+// moe_dispatch_kernel values).
+constexpr int kDispatchOneWgMaxE = 768;  // LDS of the one-work-group kernel: 18 ints per expert
 int dispatch_segment_len(int64_t A);
 int64_t dispatch_num_segments(int64_t A);
-// True when launch_dispatch runs as one work-group (small batches; MOE_DISPATCH=fused|multi
-// overrides).
-bool dispatch_fused(int64_t A, int E);
+bool dispatch_supported(int E, int path);
+// True when launch_dispatch runs as one work-group.
+bool dispatch_fused(int64_t A, int E, int path);
 // cap: rows each expert keeps (its first cap assignments in ascending id; the others get
-// inv_perm = -1 and are not counted); INT32_MAX for none.
+// inv_perm = -1 and are not counted); INT32_MAX for none.  With tiles non-null, the tile map
+// of the grouped GEMMs (M tiles of up to bm rows, one map entry each) goes to tiles and its
+// size to tile_count[0].
 hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_counts,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                           int cap, const TileSplit& ts, int32_t* tiles, int32_t* tile_count,
+                           int cap, int path, int bm, int32_t* tiles, int32_t* tile_count,
                            hipStream_t stream);
-// Tile maps from offsets alone (staged API).
-hipError_t launch_tile_map(const int32_t* offsets, int E, const TileSplit& ts, int32_t* tiles,
+// Tile map from offsets alone (staged API).
+hipError_t launch_tile_map(const int32_t* offsets, int E, int bm, int32_t* tiles,
                            int32_t* tile_count, hipStream_t stream);
 hipError_t launch_gather_rows(const void* x, int64_t D, int esize, const int32_t* perm,
                               const int32_t* offsets, int E, int K, int64_t A, void* x_perm,

@@ -1,0 +1,90 @@
+// Machine-peak probes (include/moe_peaks.h): a streaming HBM read and a register-only MFMA
+// loop.  They measure the two roofline ceilings of the layer's kernels on the running GPU, at
+// the clock it holds under that load ("S23-J10" §3: a grouped GEMM over expert weights is bound
+// by reading them when each expert sees few rows, by the matrix cores when it sees hundreds).
+#include "../../include/moe_peaks.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kReadGroups = 2048;
+constexpr int kReadThreads = 256;
+constexpr int kReadDepth = 8;  // 16-byte loads in flight per lane
+
+__global__ void __launch_bounds__(kReadThreads) hbm_read_kernel(const uint4* __restrict__ buf,
+                                                                int64_t n16,
+                                                                float* __restrict__ sink) {
+  __shared__ uint32_t part[kReadThreads / 64];
+  const int64_t stride = (int64_t)kReadGroups * kReadThreads;
+  int64_t i = (int64_t)blockIdx.x * kReadThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kReadDepth - 1) * stride < n16; i += kReadDepth * stride) {
+    uint4 v[kReadDepth];
+#pragma unroll
+    for (int k = 0; k < kReadDepth; ++k) v[k] = buf[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < kReadDepth; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = buf[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int w = 0; w < kReadThreads / 64; ++w) r ^= part[w];
+    sink[blockIdx.x] = __uint_as_float(r);
+  }
+}
+
+__global__ void __launch_bounds__(256) mfma_loop_kernel(int iters, float* __restrict__ sink) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (__bf16)((float)((lane + j + iters) & 7) * 0.125f);
+    b[j] = (__bf16)((float)((lane * 3 + j) & 7) * 0.0625f);
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[k], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s += acc[k][0] + acc[k][1] + acc[k][2] + acc[k][3];
+  if (lane == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+int moe_peak_hbm_read(const void* buf, size_t bytes, float* sink, moe_stream_t stream) {
+  if (!buf || !sink || (reinterpret_cast<uintptr_t>(buf) & 15) ||
+      (reinterpret_cast<uintptr_t>(sink) & 15) || bytes == 0 || bytes % 65536)
+    return MOE_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(moe::hbm_read_kernel, dim3(moe::kReadGroups), dim3(moe::kReadThreads), 0,
+                     (hipStream_t)stream, (const uint4*)buf, (int64_t)(bytes / 16), sink);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_peak_mfma_bf16(int waves, int iters, float* sink, moe_stream_t stream) {
+  if (!sink || (reinterpret_cast<uintptr_t>(sink) & 15) || waves <= 0 || waves % 4 ||
+      waves > 65536 || iters < 0)
+    return MOE_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(moe::mfma_loop_kernel, dim3(waves / 4), dim3(256), 0, (hipStream_t)stream,
+                     iters, sink);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -103,6 +103,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const TopkArgs a) {
     val[j] = v;
     key[j] = e < E ? ((unsigned long long)order_key(v) << 32) | (0xFFFFFFFFu - (uint32_t)e)
                    : 0ull;  // below every real key
+    if (a.keys_out && !a.sel_bias && e < E) a.keys_out[t * E + e] = v;
   }
 
   // Selection-only bias: the key becomes score + bias (score = softmax probability over all
@@ -131,9 +132,11 @@ __global__ void __launch_bounds__(256) topk_kernel(const TopkArgs a) {
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       const int e = lane + 64 * j;
-      if (e < E)
-        key[j] = ((unsigned long long)order_key(sc[j] + a.sel_bias[e]) << 32) |
-                 (0xFFFFFFFFu - (uint32_t)e);
+      if (e < E) {
+        const float kv = sc[j] + a.sel_bias[e];
+        key[j] = ((unsigned long long)order_key(kv) << 32) | (0xFFFFFFFFu - (uint32_t)e);
+        if (a.keys_out) a.keys_out[t * E + e] = kv;
+      }
     }
   }
 

@@ -177,12 +177,20 @@ def topk_select_biased(logits: Any, K: int, scoring: str, select_bias: Any) -> n
 
 
 def route(logits: Any, K: int, scoring: str = SCORING_SOFTMAX,
-          renormalize: bool = True, select_bias: Optional[Any] = None):
+          renormalize: bool = True, select_bias: Optional[Any] = None,
+          select_keys: Optional[Any] = None):
     """(topk_idx [T,K] int32, topk_w [T,K] float64) from logits.
 
     With select_bias, the experts are chosen on score + bias and weighted with the unbiased
-    scores ([Satori-1.6] §三)."""
-    if select_bias is None:
+    scores ([Satori-1.6] §三).  select_keys [T,E], if given, are the score + bias values some
+    other implementation compared (e.g. in float32): the choice is then the same total order
+    (key descending, id ascending) applied to those keys, so the two choices can be compared bit
+    for bit; the weights still come from the logits."""
+    if select_keys is not None:
+        if select_bias is None:
+            raise ValueError("select_keys are only meaningful with a select_bias")
+        idx = topk_select(select_keys, K)
+    elif select_bias is None:
         idx = topk_select(logits, K)
     else:
         idx = topk_select_biased(logits, K, scoring, select_bias)
@@ -331,6 +339,7 @@ def moe_forward(x: Any, w_router: Any, w_gate_up: Sequence[Any], w_down: Sequenc
                 w_shared_gate: Optional[Any] = None,
                 logits: Optional[Any] = None,
                 select_bias: Optional[Any] = None,
+                select_keys: Optional[Any] = None,
                 capacity: Optional[int] = None) -> Dict[str, Any]:
     """Forward pass of one MoE layer, float64, without the residual.
 
@@ -341,6 +350,7 @@ def moe_forward(x: Any, w_router: Any, w_gate_up: Sequence[Any], w_down: Sequenc
     logits: if given (e.g. fp32 logits exported by another implementation), routing is taken
     from them instead of being recomputed from x and w_router.
     select_bias: [E] selection-only bias ([Satori-1.6] §三), or None.
+    select_keys: [T,E] score + bias values to choose on (see route), or None.
     capacity: rows per expert (see expert_capacity); dropped assignments contribute nothing.
 
     y_t = Σ_k α_{t,k} · E_{I_t[k]}(x_t) + g_t · E_s(x_t)
@@ -352,7 +362,7 @@ def moe_forward(x: Any, w_router: Any, w_gate_up: Sequence[Any], w_down: Sequenc
     else:
         r = as_f64(logits)
     E = r.shape[1]
-    idx, alpha = route(r, K, scoring, renormalize, select_bias)
+    idx, alpha = route(r, K, scoring, renormalize, select_bias, select_keys)
     d = dispatch(idx, E, capacity)
     counts, offsets, perm, inv_perm = d["counts"], d["offsets"], d["perm"], d["inv_perm"]
 

@@ -44,13 +44,14 @@ class LazyRows:
 
 
 def problem_for(cfg: LayerConfig, T=None, out_dtype=None, atomic_combine=False,
-                renormalize=True):
+                renormalize=True, gemm_kernel="auto", dispatch_kernel="auto"):
     dt = cfg.torch_dtype
     return abi.make_problem(T=cfg.T if T is None else T, D=cfg.D, E=cfg.E, K=cfg.K, F=cfg.F,
                             F_shared=cfg.F_shared, shared_gated=cfg.shared_gated,
                             scoring=cfg.scoring, dtype=dt,
                             out_dtype=dt if out_dtype is None else out_dtype,
-                            atomic_combine=atomic_combine, renormalize=renormalize)
+                            atomic_combine=atomic_combine, renormalize=renormalize,
+                            gemm_kernel=gemm_kernel, dispatch_kernel=dispatch_kernel)
 
 
 def weights_for(layer) -> dict:

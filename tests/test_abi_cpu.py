@@ -14,13 +14,17 @@ import pytest
 from mixture_experts_layer_renorm_amd import abi
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe.h")
+INCLUDE = os.path.join(ROOT, "include")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 
 
 def _declared_functions():
-    text = open(HEADER, encoding="utf-8").read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = open(h, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -49,9 +53,11 @@ def test_struct_layout_matches_c(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
-        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(moe_problem),"
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n\", sizeof(moe_problem),"
         " offsetof(moe_problem, flags), offsetof(moe_problem, out_dtype), sizeof(moe_weights),"
-        " sizeof(moe_routing), offsetof(moe_routing, shared_gate));return 0;}\n")
+        " sizeof(moe_routing), offsetof(moe_routing, shared_gate),"
+        " offsetof(moe_problem, gemm_kernel), offsetof(moe_problem, dispatch_kernel),"
+        " offsetof(moe_routing, select_keys));return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o",
                     str(exe)], check=True)
@@ -59,15 +65,51 @@ def test_struct_layout_matches_c(tmp_path):
                                           check=True).stdout.split()]
     want = [ctypes.sizeof(abi.moe_problem), abi.moe_problem.flags.offset,
             abi.moe_problem.out_dtype.offset, ctypes.sizeof(abi.moe_weights),
-            ctypes.sizeof(abi.moe_routing), abi.moe_routing.shared_gate.offset]
+            ctypes.sizeof(abi.moe_routing), abi.moe_routing.shared_gate.offset,
+            abi.moe_problem.gemm_kernel.offset, abi.moe_problem.dispatch_kernel.offset,
+            abi.moe_routing.select_keys.offset]
     assert got == want
 
 
-def _prob(**kw):
+def _prob(dtype="f32", **kw):
     base = dict(T=64, D=256, E=8, K=2, F=128)
     base.update(kw)
     import torch
-    return abi.make_problem(**base, dtype=torch.float32)
+    return abi.make_problem(**base, dtype=torch.float32 if dtype == "f32" else torch.bfloat16)
+
+
+def _plan(**kw):
+    return abi.describe_plan(_prob(**kw))
+
+
+def test_plan_choices_and_32bit_offset_limits():
+    """The plan moe_forward launches, read through moe_describe_plan (no GPU).  The matrix-core
+    GEMM addresses operands with 32-bit byte offsets, so a bf16 operand of 4 GiB or more must
+    send that GEMM to the 64-bit tile GEMM: the grouped GEMMs when T*K*max(D,F) or one expert's
+    weights reach 4 GiB, the shared expert's when x [T,D], Hs [T,F_s] or its weights do."""
+    sig = dict(dtype="bf16", T=16384, D=4096, E=256, K=6, F=2048, F_shared=2048)
+    text = _plan(**sig)
+    assert "grouped gate_up/down: mfma 256x256" in text and "shared: mfma 256x256" in text
+    assert "fp16 rows" in text
+    # x is [2^19, 4096] bf16 = 4 GiB exactly: both GEMM kinds leave the matrix-core kernel
+    big = dict(dtype="bf16", T=1 << 19, D=4096, E=8, K=1, F=256, F_shared=1024)
+    text = _plan(**big)
+    assert "grouped gate_up/down: tile 256x128" in text, text
+    assert "shared: tile 256x128" in text, text
+    # one token fewer fits both
+    text = _plan(**dict(big, T=(1 << 19) - 1))
+    assert "grouped gate_up/down: mfma" in text and "shared: mfma" in text, text
+    # shared weights [2 F_s, D] of 4 GiB (F_s = 2^18, D = 4096) with a small batch of tokens that
+    # still fills the chip
+    text = _plan(dtype="bf16", T=4096, D=4096, E=8, K=1, F=256, F_shared=1 << 18)
+    assert "shared: tile 256x128" in text, text
+    # fp32 layers never take the matrix-core GEMM; forced tiles are reported
+    assert "grouped gate_up/down: tile 32x128" in _plan(T=64)
+    assert "grouped gate_up/down: tile 256x128" in _plan(T=64, gemm_kernel="tile256")
+    assert "grouped gate_up/down: tile 32x128" in _plan(dtype="bf16", T=64, gemm_kernel="tile32")
+    assert "one work-group" in _plan(T=64)
+    assert "scan+scatter" in _plan(T=64, dispatch_kernel="multi")
+    assert "one work-group" in _plan(T=100000, dispatch_kernel="one_workgroup")
 
 
 def _ws_size(lib, p):
@@ -98,6 +140,17 @@ def test_workspace_size_and_validation(lib):
     assert _ws_size(lib, _prob(capacity_factor=1.25, min_capacity=-3))[0] == \
         abi.MOE_ERR_INVALID_ARG
     assert _ws_size(lib, _prob(capacity_factor=1.25, min_capacity=4))[0] == abi.MOE_OK
+    # kernel-plan fields: unknown values; the matrix-core GEMM forced on an fp32 layer; the
+    # one-work-group dispatch forced past its expert limit
+    for field in ("gemm_kernel", "dispatch_kernel"):
+        for bad in (-1, 9):
+            pb = _prob()
+            setattr(pb, field, bad)
+            assert _ws_size(lib, pb)[0] == abi.MOE_ERR_INVALID_ARG
+    assert _ws_size(lib, _prob(gemm_kernel="mfma"))[0] == abi.MOE_ERR_UNSUPPORTED
+    assert _ws_size(lib, _prob(E=1000, K=4, dispatch_kernel="one_workgroup"))[0] == \
+        abi.MOE_ERR_UNSUPPORTED
+    assert _ws_size(lib, _prob(E=768, K=4, dispatch_kernel="one_workgroup"))[0] == abi.MOE_OK
     assert lib.moe_workspace_size(None, None) == abi.MOE_ERR_INVALID_ARG
     assert b"NULL" in lib.moe_last_error()
     # the workspace grows with T; the atomic combine needs no [T*K, D] row buffer
@@ -105,6 +158,16 @@ def test_workspace_size_and_validation(lib):
     pa = _prob()
     pa.flags = abi.MOE_FLAG_ATOMIC_COMBINE
     assert _ws_size(lib, pa)[1] < _ws_size(lib, _prob())[1]
+
+
+def test_peak_probes_validate_before_launch(lib):
+    assert lib.moe_peak_hbm_read(None, 65536, ALIGNED, None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_peak_hbm_read(ALIGNED, 65536 + 16, ALIGNED, None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_peak_hbm_read(ALIGNED + 4, 65536, ALIGNED, None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_peak_hbm_read(ALIGNED, 0, ALIGNED, None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_peak_mfma_bf16(6, 10, ALIGNED, None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_peak_mfma_bf16(0, 10, ALIGNED, None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_peak_mfma_bf16(8, 10, None, None) == abi.MOE_ERR_INVALID_ARG
 
 
 def test_status_strings(lib):

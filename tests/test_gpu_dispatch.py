@@ -12,10 +12,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run_dispatch(idx: torch.Tensor, E: int, x=None, D=64, capacity_factor=0.0, min_capacity=0):
+def _run_dispatch(idx: torch.Tensor, E: int, x=None, D=64, capacity_factor=0.0, min_capacity=0,
+                  path="auto"):
     T, K = idx.shape
     p = abi.make_problem(T=T, D=D, E=E, K=K, F=64, capacity_factor=capacity_factor,
-                         min_capacity=min_capacity)
+                         min_capacity=min_capacity, dispatch_kernel=path)
     r = abi.alloc_routing(p, DEV, logits=False)
     r["topk_idx"] = idx.to(DEV, torch.int32).contiguous()
     x_perm = None
@@ -26,8 +27,8 @@ def _run_dispatch(idx: torch.Tensor, E: int, x=None, D=64, capacity_factor=0.0, 
     return r, x_perm
 
 
-def _check(idx: torch.Tensor, E: int):
-    r, _ = _run_dispatch(idx, E)
+def _check(idx: torch.Tensor, E: int, path="auto"):
+    r, _ = _run_dispatch(idx, E, path=path)
     want = O.dispatch(i64(idx), E)
     n = int(want["offsets"][E])
     np.testing.assert_array_equal(i64(r["expert_counts"]), want["counts"])
@@ -92,30 +93,28 @@ def test_dispatch_deterministic():
 
 # Both dispatch implementations (one work-group for small batches; count/scan/scatter kernels
 # otherwise) forced on the same inputs, inside and outside their default ranges.
-@pytest.mark.parametrize("path", ["fused", "multi"])
+@pytest.mark.parametrize("path", ["one_workgroup", "multi"])
 @pytest.mark.parametrize("T,E,K", [(1, 1, 1), (64, 256, 8), (1023, 7, 3), (4096, 256, 8),
                                    (2000, 768, 9), (20000, 64, 64)])
-def test_dispatch_both_paths(monkeypatch, path, T, E, K):
-    monkeypatch.setenv("MOE_DISPATCH", path)
+def test_dispatch_both_paths(path, T, E, K):
     g = torch.Generator().manual_seed(100 + T + E + K)
     idx = _topk_like(T, E, K, g)
     if T > 1:
         idx[torch.rand(idx.shape, generator=g) < 0.05] = -1  # sentinels
-    _check(idx, E)
+    _check(idx, E, path)
 
 
 # Expert capacity: each expert keeps its first C assignments; the rest are dropped.
-@pytest.mark.parametrize("path", ["fused", "multi"])
+@pytest.mark.parametrize("path", ["one_workgroup", "multi"])
 @pytest.mark.parametrize("T,E,K,cf,minc", [(64, 8, 2, 1.0, 0), (1023, 7, 3, 0.5, 0),
                                            (4096, 256, 8, 1.25, 4), (3000, 128, 4, 1.0, 40),
                                            (20000, 64, 8, 1.1, 0), (50, 16, 4, 0.01, 0)])
-def test_dispatch_capacity(monkeypatch, path, T, E, K, cf, minc):
-    monkeypatch.setenv("MOE_DISPATCH", path)
+def test_dispatch_capacity(path, T, E, K, cf, minc):
     g = torch.Generator().manual_seed(200 + T + E)
     hot = [i * max(1, E // 8) for i in range(min(8, E))]
     idx = _topk_like(T, E, K, g, hot, 0.3)  # skewed, so hot experts overflow
     idx[torch.rand(idx.shape, generator=g) < 0.03] = -1
-    r, _ = _run_dispatch(idx, E, capacity_factor=cf, min_capacity=minc)
+    r, _ = _run_dispatch(idx, E, capacity_factor=cf, min_capacity=minc, path=path)
     C = O.expert_capacity(T * K, E, float(np.float32(cf)), minc)
     want = O.dispatch(i64(idx), E, C)
     assert want["dropped"] > 0

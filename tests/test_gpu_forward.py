@@ -64,8 +64,8 @@ def _case(name):
     return cfg, layer, T
 
 
-def _forward(cfg, layer, T, out_dtype, atomic):
-    p = problem_for(cfg, T=T, out_dtype=out_dtype, atomic_combine=atomic)
+def _forward(cfg, layer, T, out_dtype, atomic, gemm_kernel="auto"):
+    p = problem_for(cfg, T=T, out_dtype=out_dtype, atomic_combine=atomic, gemm_kernel=gemm_kernel)
     r = abi.alloc_routing(p, DEV)
     out = torch.empty((T, cfg.D), dtype=out_dtype, device=DEV)
     abi.moe_forward(p, layer["x"], weights_for(layer), r, out, abi.alloc_workspace(p, DEV))
@@ -170,19 +170,18 @@ def test_concentrated_routing_hits_eight_experts():
     assert np.all(counts[hot_experts(cfg)] == T)
 
 
-GROUPED_TILES = ["small", "large", "stream64", "stream128", "stream192", "mfma", "split192"]
+GROUPED_TILES = ["tile32", "tile256", "mfma"]
 
 
 @pytest.mark.parametrize("tile", GROUPED_TILES)
 @pytest.mark.parametrize("name", ["a3b_E16", "a17b_E32", "skew_conc_E64", "ds_sigmoid_E16",
                                   "a3b_T1", "odd_k", "skew_E64"])
-def test_every_grouped_tile_shape_matches_oracle(name, tile, monkeypatch):
-    """The library picks the grouped GEMM's tile from the mean rows per expert; forcing each
-    shape on the same inputs covers ragged groups, multi-tile experts and empty experts in all."""
-    monkeypatch.setenv("MOE_GROUPED_TILE", tile)
+def test_every_grouped_tile_shape_matches_oracle(name, tile):
+    """Every grouped GEMM the library has, forced through moe_problem.gemm_kernel on the same
+    inputs: ragged groups, multi-tile experts and empty experts in all of them."""
     cfg, layer, T = _case(name)
     for atomic in (False, True):
-        out32, r = _forward(cfg, layer, T, torch.float32, atomic)
+        out32, r = _forward(cfg, layer, T, torch.float32, atomic, gemm_kernel=tile)
         ref = _oracle(cfg, layer, r["logits"])
         _check_routing(cfg, r, ref)
         err = rel_max_err(out32, ref["out"])
@@ -192,20 +191,22 @@ def test_every_grouped_tile_shape_matches_oracle(name, tile, monkeypatch):
 @pytest.mark.parametrize("name", ["ds_sigmoid_E16", "a3b_E16", "a3b_decode"])
 def test_forward_with_select_bias(name):
     """moe_forward with a selection-only bias: routing bit-exact against the oracle fed the
-    GPU's logits and the same bias, output within the layer's tolerance."""
+    GPU's logits and the fp32 selection keys (score + bias) the GPU compared, output within the
+    layer's tolerance."""
     cfg, layer, T = _case(name)
     g = torch.Generator(device="cpu").manual_seed(77)
     scale = 0.05 if cfg.scoring == "sigmoid" else 2.0 / cfg.E
     bias = (torch.randn(cfg.E, generator=g) * scale).to(torch.float32)
     p = problem_for(cfg, T=T, out_dtype=torch.float32)
-    r = abi.alloc_routing(p, DEV)
+    r = abi.alloc_routing(p, DEV, select_keys=True)
     out = torch.empty((T, cfg.D), dtype=torch.float32, device=DEV)
     w = weights_for(layer)
     w["select_bias"] = bias.to(DEV)
     abi.moe_forward(p, layer["x"], w, r, out, abi.alloc_workspace(p, DEV))
     torch.cuda.synchronize()
     args, kw = oracle_args(cfg, layer)
-    ref = O.moe_forward(*args, logits=f64(r["logits"]), select_bias=f64(bias), **kw)
+    ref = O.moe_forward(*args, logits=f64(r["logits"]), select_bias=f64(bias),
+                        select_keys=f64(r["select_keys"]), **kw)
     _check_routing(cfg, r, ref)
     plain = O.topk_select(f64(r["logits"]), cfg.K)
     assert np.any(np.sort(ref["topk_idx"], 1) != np.sort(plain, 1))  # the bias mattered
@@ -218,10 +219,14 @@ def test_forward_with_select_bias(name):
 def test_forward_with_capacity(name, cf, atomic):
     """Token dropping: routing and the kept rows bit-exact against the oracle with the same
     capacity, dropped slots contributing nothing (a token with every slot dropped and no shared
-    expert outputs exactly 0), output within the layer's tolerance.  The tolerance is taken on
-    the scale of the layer's dropless output: dropping removes terms (on the skewed layer most
-    of the large hot-expert ones), which shrinks the output RMS but not the rounding of the
-    terms that remain."""
+    expert outputs exactly 0).  Output bound: 2e-2 (bf16) / 1e-4 (fp32) of the output RMS,
+    applied token by token on each token's own output RMS (every case) and on the RMS of the
+    whole capped output (every case but the skewed layer).  On the skewed layer dropping
+    removes most hot-expert terms: the output RMS falls 2.4x while the tokens that kept their
+    hot slots stay as large, so max|y|/RMS grows from about 7 to 13-19 and the rounding of H
+    to bf16 alone (the intermediate precision of the pages' chain) reaches 2.3-3.2e-2 of that
+    RMS in a float64 emulation of five draws, while staying within 0.9-1.1e-2 of each token's
+    own RMS."""
     cfg, layer, T = _case(name)
     p = problem_for(cfg, T=T, out_dtype=torch.float32, atomic_combine=atomic)
     p.capacity_factor = cf
@@ -234,10 +239,16 @@ def test_forward_with_capacity(name, cf, atomic):
     ref = O.moe_forward(*args, logits=f64(r["logits"]), capacity=C, **kw)
     _check_routing(cfg, r, ref)
     assert int(ref["counts"].max()) <= C
-    full = O.moe_forward(*args, logits=f64(r["logits"]), **kw)["out"]
-    scale = float(np.sqrt(np.mean(full ** 2)))
-    err = float(np.max(np.abs(f64(out) - ref["out"]))) / scale
-    assert err <= _tol(cfg), f"{name}: max|err|/RMS(dropless) = {err:.3e}"
+    got, want = f64(out), ref["out"]
+    err = rel_max_err(got, want)
+    tok_rms = np.sqrt(np.mean(want ** 2, axis=1))
+    live = tok_rms > 0
+    per_tok = float(np.max(np.max(np.abs(got - want), axis=1)[live] / tok_rms[live]))
+    print(f"{name} cf={cf} atomic={atomic}: max|err|/RMS(capped output) = {err:.3e}, "
+          f"max over tokens of max|err_t|/RMS(y_t) = {per_tok:.3e}")
+    assert per_tok <= _tol(cfg), f"{name}: per-token max|err_t|/RMS(y_t) = {per_tok:.3e}"
+    if name != "skew_E64":
+        assert err <= _tol(cfg), f"{name}: max|err|/RMS = {err:.3e}"
     all_dropped = np.all(ref["inv_perm"].reshape(T, cfg.K) < 0, axis=1)
     if not cfg.F_shared and all_dropped.any():
         assert np.all(f64(out)[all_dropped] == 0.0)

@@ -148,20 +148,36 @@ def test_router_gemm_and_topk(name, T):
 
 # ---- selection-only bias ("1.6 ..." §三): choose on score + bias, weight with the score ----
 
-def _near_tie_ok(keys64, got_idx, want_idx, K, delta):
-    """Tokens whose GPU and oracle choices differ must have the oracle's K-th and (K+1)-th
-    keys within delta (the fp32 score's rounding against the float64 one)."""
-    differ = np.nonzero(np.any(np.sort(got_idx, 1) != np.sort(want_idx, 1), axis=1))[0]
-    for t in differ:
-        srt = np.sort(keys64[t])[::-1]
-        assert srt[K - 1] - srt[K] <= delta, (t, srt[K - 1] - srt[K])
-    return differ
+def select_key_bound(logits64, bias64, scoring, E):
+    """Largest error of the GPU's fp32 key fl(score) + bias against the float64 score + bias.
+
+    sigmoid: s = 1/(1 + e^-r) from a float32 exp (a few ulp), an add and a divide: relative
+    error within 8u.  softmax: p = e^(r - m) / sum over E of e^(r_j - m): the subtraction errs
+    by u|r - m| before the exp (relative u|r - m| after it), the exp by a few ulp, the float32
+    sum over E terms by at most (E/64 + 6) u relative (lane sums of E/64 terms, then a 6-level
+    butterfly), and the divide by u; with the largest |r_j - m| of the row, the relative error
+    of p is within (2 |r - m| + 2 max|r_j - m| + E/64 + 16) u.  The final add of the bias rounds
+    once more (u |key|), counted twice for slack."""
+    u = 2.0 ** -24
+    score = O.routing_scores(logits64, scoring)
+    key = np.abs(score + bias64[None, :])
+    if scoring == "sigmoid":
+        rel = 8 * u
+    else:
+        z = logits64 - np.max(logits64, axis=1, keepdims=True)
+        rel = (2 * np.abs(z) + 2 * np.max(np.abs(z), axis=1, keepdims=True) + E / 64 + 16) * u
+    return rel * score + 2 * u * key + 1e-30
 
 
 @pytest.mark.parametrize("E,K", [(8, 2), (256, 8), (256, 6), (64, 64), (130, 3), (1024, 16)])
 @pytest.mark.parametrize("scoring", ["softmax", "sigmoid"])
 @pytest.mark.parametrize("renormalize", [True, False])
 def test_topk_select_bias(E, K, scoring, renormalize):
+    """Routing with a selection-only bias is bit-exact: the oracle chooses on the fp32 keys
+    (score + bias) the GPU compared, exported through select_keys, so both sides apply the same
+    total order to the same values and no token may differ.  The keys themselves are checked
+    against the float64 score + bias within their rounding bound, and the weights (unbiased
+    scores of the chosen experts) within 1e-6."""
     g = torch.Generator().manual_seed(E * 7 + K)
     T = 700
     logits = torch.randn((T, E), generator=g) * 1.5
@@ -170,25 +186,35 @@ def test_topk_select_bias(E, K, scoring, renormalize):
     bias = (torch.randn(E, generator=g) * scale).to(torch.float32)
     p = abi.make_problem(T=T, D=64, E=E, K=K, F=64, scoring=scoring, renormalize=renormalize)
     r = {"topk_idx": torch.empty((T, K), dtype=torch.int32, device=DEV),
-         "topk_w": torch.empty((T, K), dtype=torch.float32, device=DEV)}
+         "topk_w": torch.empty((T, K), dtype=torch.float32, device=DEV),
+         "select_keys": torch.empty((T, E), dtype=torch.float32, device=DEV)}
     abi.moe_route_logits(p, logits.to(DEV), r, select_bias=bias.to(DEV))
     torch.cuda.synchronize()
     L, b = f64(logits), f64(bias)
+    keys = f64(r["select_keys"])
     got = i64(r["topk_idx"])
-    want = O.topk_select_biased(L, K, scoring, b)
-    if K < E:
-        keys = O.routing_scores(L, scoring) + b[None, :]
-        differ = _near_tie_ok(keys, got, want, K, delta=1e-6)
-        assert len(differ) <= max(1, T // 100)
-    else:
-        differ = np.array([], dtype=np.int64)
-    same = np.setdiff1d(np.arange(T), differ)
-    np.testing.assert_array_equal(got[same], want[same])
-    want_w = O.routing_weights(L, want, scoring, renormalize)
-    np.testing.assert_allclose(f64(r["topk_w"])[same], want_w[same], rtol=0, atol=TOL_ROUTING_W)
+    want, want_w = O.route(L, K, scoring, renormalize, select_bias=b, select_keys=keys)
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_allclose(f64(r["topk_w"]), want_w, rtol=0, atol=TOL_ROUTING_W)
+    keys64 = O.routing_scores(L, scoring) + b[None, :]
+    assert np.all(np.abs(keys - keys64) <= select_key_bound(L, b, scoring, E))
     # the bias moved the choice of many tokens away from the unbiased router's
     if K < E:
         assert np.mean(np.any(np.sort(got, 1) != np.sort(O.topk_select(L, K), 1), axis=1)) > 0.05
+
+
+def test_select_keys_without_bias_are_the_logits():
+    """Without a selection bias the key top-K compares is the logit itself."""
+    g = torch.Generator().manual_seed(5)
+    T, E, K = 99, 130, 5
+    logits = torch.randn((T, E), generator=g)
+    p = abi.make_problem(T=T, D=64, E=E, K=K, F=64)
+    r = {"topk_idx": torch.empty((T, K), dtype=torch.int32, device=DEV),
+         "topk_w": torch.empty((T, K), dtype=torch.float32, device=DEV),
+         "select_keys": torch.empty((T, E), dtype=torch.float32, device=DEV)}
+    abi.moe_route_logits(p, logits.to(DEV), r)
+    torch.cuda.synchronize()
+    assert torch.equal(r["select_keys"].cpu(), logits)
 
 
 @pytest.mark.parametrize("E", [1, 7, 256, 1024])

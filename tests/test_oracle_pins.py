@@ -110,6 +110,38 @@ def test_selection_bias_invariants(scoring):
     np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-14)
 
 
+def test_route_on_given_selection_keys():
+    """route(select_keys=...) chooses on keys computed elsewhere (e.g. a float32 score + bias)
+    and still weights with the unbiased scores of the logits.  On the worked example with the
+    +0.45 bias, keys equal to score + bias reproduce the biased choice {2, 4}; keys that put
+    expert 5 (1-based) above expert 4 move the choice to {2, 5} and its weights to the page's
+    0.60 / 0.40 -- so a caller-supplied key really decides the set."""
+    g = _golden("worked_example_e5_k2.json")
+    s = np.array(g["scores"])
+    logits = np.log(s / (1.0 - s))[None, :]
+    b = np.array([0.0, 0.0, 0.0, 0.45, 0.0])
+    keys = s[None, :] + b
+    idx, w = O.route(logits, g["k"], O.SCORING_SIGMOID, select_bias=b, select_keys=keys)
+    assert [i + 1 for i in idx[0]] == [2, 4]
+    np.testing.assert_allclose(w[0], [0.75, 0.25], rtol=0, atol=1e-15)
+    swapped = keys.copy()
+    swapped[0, 4] = swapped[0, 3] + 0.01
+    idx, w = O.route(logits, g["k"], O.SCORING_SIGMOID, select_bias=b, select_keys=swapped)
+    assert [i + 1 for i in idx[0]] == g["selected_1based"]
+    np.testing.assert_allclose(w[0], g["weights"], rtol=0, atol=1e-15)
+    # float32-rounded keys of random rows choose what the float64 rule chooses, except where
+    # rounding can reorder (gaps below the float32 spacing); equal float32 keys tie to the
+    # lower id
+    rng = np.random.default_rng(41)
+    r = rng.standard_normal((200, 16))
+    bb = rng.standard_normal(16) * 0.05
+    k32 = (O.routing_scores(r, O.SCORING_SIGMOID) + bb).astype(np.float32)
+    idx32, _ = O.route(r, 4, O.SCORING_SIGMOID, select_bias=bb, select_keys=k32)
+    np.testing.assert_array_equal(idx32, O.topk_select(k32, 4))
+    with pytest.raises(ValueError):
+        O.route(r, 4, O.SCORING_SIGMOID, select_keys=k32)
+
+
 def test_update_select_bias_feedback():
     """Loads 10, 2, 5, 3 (mean 5): the overloaded expert's bias drops by gamma, the two
     underloaded ones rise by gamma, the one at the mean is unchanged ([Satori-1.6] §三)."""
