@@ -5,10 +5,22 @@ One step = one moe_forward call (router GEMM, top-K, dispatch, grouped gate_up G
 SiLU*up, shared expert, grouped down GEMM, weighted gather combine with the final cast) over one
 synthetic batch already resident in HBM.
 
-Default workload: the 35B-A3B-shaped layer (D=2048, E=256, top-8, F=512, bf16) at the prefill
-batch T=4096; the same layer's decode batch T=64 is timed next to it.  Prints one JSON line.
+Headline workload: the DeepSeek-style sigmoid layer (T=16384, D=4096, E=256, top-6, F=2048, one
+ungated shared expert F=2048, bf16), the largest of the layer configurations that fits one GPU.
+Its dominant kernel, the routed gate_up GEMM, is bound by the matrix cores, so the roofline
+object is TFLOP/s against the dense bf16 peak.  Every other configuration (tiny fp32, the
+35B-A3B-shaped decode and prefill batches, the 397B-A17B-shaped layer, the skewed and fully
+concentrated layers, the granularity pair) gets its own entry under "workloads".
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload a3b_prefill]
+Timing protocol, per workload: W warm-up steps, then K timed steps.  Before each step a 1 GiB
+buffer is read once (evicts the L2s and the 256 MiB MALL, so weights come from HBM every step,
+as they would between the layers of a model; a read leaves no dirty lines whose write-back
+would fall into the next step); HIP events on the launch stream bracket the step and its routed
+gate_up launch.  ms_per_step is the median over the K steps.  The machine
+peaks are measured live (a streaming read and a register-only MFMA loop) and reported beside
+the published ones.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload ds_sigmoid]
 """
 
 from __future__ import annotations
@@ -18,6 +30,7 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -30,6 +43,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 # taken on exactly these)
 _CSRC = os.path.join(ROOT, "mixture_experts_layer_renorm_amd", "csrc")
 GEMM_SRCS = [os.path.join(_CSRC, f) for f in ("gemm_mfma.hip", "kernels.h", "silu.h")]
+
+ALL_WORKLOADS = ("ds_sigmoid", "tiny", "a3b_decode", "a3b_prefill", "a17b", "skew", "skew_conc",
+                 "gran_e128", "gran_e64")
+FLUSH_BYTES = 1 << 30
 
 
 def gemm_source_sha256() -> str:
@@ -44,22 +61,26 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="a3b_prefill")
-    ap.add_argument("--decode-workload", default="a3b_decode")
-    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--workload", default="ds_sigmoid", help="headline workload")
+    ap.add_argument("--workloads", default="all",
+                    help="comma-separated list of the other workloads to time, 'all' or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mfma-workload", default="ds_sigmoid",
-                    help="matrix-core-bound workload reported beside the main one")
-    ap.add_argument("--no-mfma-workload", action="store_true")
-    ap.add_argument("--no-granularity", action="store_true",
-                    help="skip the granularity pair (128 experts x F=1536 x top-8 vs "
-                         "64 x 3072 x top-4)")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-chunk", type=int, default=1024,
+                    help="tokens per oracle call in the CPU baseline")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not read 1 GiB between steps (weights may stay in the MALL)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured machine peaks")
     ap.add_argument("--atomic-combine", action="store_true",
                     help="time the fused fp32-atomic combine instead of the default gather")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one 1 GiB device-to-device copy (for PMC scaling)")
     return ap.parse_args()
+
+
+def progress(**kw):
+    sys.stderr.write(json.dumps({"progress": kw}) + "\n")
+    sys.stderr.flush()
 
 
 class HipEvents:
@@ -68,6 +89,7 @@ class HipEvents:
     def __init__(self):
         self.lib = ctypes.CDLL("libamdhip64.so.7")
         self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -77,6 +99,10 @@ class HipEvents:
         if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
             raise RuntimeError("hipEventCreate failed")
         return e.value
+
+    def record(self, e: int, stream: int) -> None:
+        if self.lib.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a: int, b: int) -> float:
         ms = ctypes.c_float()
@@ -88,7 +114,58 @@ class HipEvents:
         self.lib.hipEventDestroy(e)
 
 
-def run_workload(name, steps, warmup, atomic_combine, hip):
+def measure_peaks(hip, reps=5):
+    """Measured HBM read rate and bf16 MFMA rate on this GPU (median of `reps` timed launches,
+    each long enough for the clock to settle under the load)."""
+    import torch
+    from mixture_experts_layer_renorm_amd import abi
+    stream = torch.cuda.current_stream().cuda_stream
+    nbytes = 4 << 30  # far beyond the 256 MiB MALL
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(65536, dtype=torch.float32, device="cuda")
+    waves, iters = 2048, 40000  # 8 waves per CU; 10.7 TFLOP per launch (about 5 ms)
+    mfma_flops = waves * iters * 8 * 16384
+    res = {}
+    for name, launch, work in (
+            ("hbm_read", lambda: abi.moe_peak_hbm_read(buf, sink), nbytes),
+            ("mfma_bf16", lambda: abi.moe_peak_mfma_bf16(waves, iters, sink), mfma_flops)):
+        launch()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            a, b = hip.create(), hip.create()
+            hip.record(a, stream)
+            launch()
+            hip.record(b, stream)
+            torch.cuda.synchronize()
+            times.append(hip.elapsed_ms(a, b))
+            hip.destroy(a)
+            hip.destroy(b)
+        ms = statistics.median(times)
+        res[name] = (ms, work / (ms / 1e3))
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"hbm_read_gbs": res["hbm_read"][1] / 1e9, "hbm_read_bytes": nbytes,
+            "hbm_read_ms": res["hbm_read"][0],
+            "mfma_bf16_tflops": res["mfma_bf16"][1] / 1e12, "mfma_bf16_ms": res["mfma_bf16"][0],
+            "mfma_loop": f"{waves} waves x {iters} x 8 v_mfma_f32_16x16x32_bf16 on registers"}
+
+
+def kernel_roofline(flops, nbytes, ms, mfma_peak_tflops, costmodel):
+    """Achieved rate of one kernel against the roofline its intensity puts it under (the
+    matrix-core peak of its dtype, or HBM)."""
+    s = ms / 1e3
+    tflops = flops / s / 1e12
+    gbs = nbytes / s / 1e9
+    ridge = mfma_peak_tflops * 1e12 / (costmodel.HBM_PEAK_GBS * 1e9)
+    bound = "mfma" if flops / nbytes >= ridge else "hbm"
+    frac = tflops / mfma_peak_tflops if bound == "mfma" else gbs / costmodel.HBM_PEAK_GBS
+    return {"ms": ms, "alg_flops": flops, "alg_bytes": nbytes, "tflops": tflops, "gbs": gbs,
+            "bound": bound, "frac": frac, "mfma_peak_tflops": mfma_peak_tflops}
+
+
+def run_workload(name, steps, warmup, atomic_combine, flush, hip):
     import torch
     from mixture_experts_layer_renorm_amd import abi, costmodel
     from mixture_experts_layer_renorm_amd.synth import CONFIGS, make_layer
@@ -107,73 +184,91 @@ def run_workload(name, steps, warmup, atomic_combine, hip):
     out = torch.empty((cfg.T, cfg.D), dtype=cfg.torch_dtype, device=dev)
     ws = abi.alloc_workspace(p, dev)
     x = layer["x"]
+    stream = torch.cuda.current_stream().cuda_stream
 
-    for _ in range(warmup):
+    def do_flush(k):
+        if flush is not None:
+            abi.moe_peak_hbm_read(flush[0], flush[1])
+
+    for k in range(warmup):
+        do_flush(k)
         abi.moe_forward(p, x, weights, routing, out, ws)
     torch.cuda.synchronize()
 
-    # Timed region: the forward as a caller runs it, with one pair of HIP events on its stream
-    # bracketing the routed gate_up launch(es) of each step (the roofline's kernel).
+    # Timed steps: events on the launch stream at the step's start, around the routed gate_up
+    # launch and at its end (moe_forward_timed records them between the launches).
     n_ev = abi.MOE_STAGE_COUNT + 1
-    gu_ev = [[hip.create(), hip.create()] for _ in range(steps)]
+    G = abi.MOE_STAGE_GATE_UP
+    ev = [[hip.create() for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
-        ev = [None] * n_ev
-        ev[abi.MOE_STAGE_GATE_UP], ev[abi.MOE_STAGE_GATE_UP + 1] = gu_ev[k]
-        abi.moe_forward_timed(p, x, weights, routing, out, ws, ev)
+        do_flush(k)
+        e = [None] * n_ev
+        e[0], e[G], e[G + 1], e[n_ev - 1] = ev[k]
+        abi.moe_forward_timed(p, x, weights, routing, out, ws, e)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    gate_up_live_ms = sum(hip.elapsed_ms(a, b) for a, b in gu_ev) / steps
-    for pair in gu_ev:
-        for e in pair:
-            hip.destroy(e)
+    step_ms = [hip.elapsed_ms(a, d) for a, _, _, d in ev]
+    gu_ms = [hip.elapsed_ms(b, c) for _, b, c, _ in ev]
+    for row in ev:
+        for h in row:
+            hip.destroy(h)
 
-    # Per-stage breakdown from a second pass with HIP events between the stages (each marker
-    # adds a few microseconds, so these stages sum to more than the plain step).
+    # Per-stage breakdown from a second pass with events between all stages (each boundary
+    # costs a few microseconds, so these stages add up to slightly more than the plain step).
     events = [[hip.create() for _ in range(n_ev)] for _ in range(steps)]
     torch.cuda.synchronize()
     for k in range(steps):
+        do_flush(k)
         abi.moe_forward_timed(p, x, weights, routing, out, ws, events[k])
     torch.cuda.synchronize()
-
-    stage_ms = [0.0] * abi.MOE_STAGE_COUNT
-    for k in range(steps):
-        for i in range(abi.MOE_STAGE_COUNT):
-            stage_ms[i] += hip.elapsed_ms(events[k][i], events[k][i + 1]) / steps
-    gpu_ms = hip.elapsed_ms(events[0][0], events[-1][-1]) / steps
+    stage_ms = {}
+    for i, sname in enumerate(abi.MOE_STAGE_NAMES):
+        stage_ms[sname] = statistics.median(
+            hip.elapsed_ms(events[k][i], events[k][i + 1]) for k in range(steps))
     for row in events:
-        for e in row:
-            hip.destroy(e)
+        for h in row:
+            hip.destroy(h)
 
     counts = routing["expert_counts"].cpu()
     U = int((counts > 0).sum())
     nz = counts[counts > 0].float()
-    ms_per_step = (t1 - t0) * 1e3 / steps
-    A = cfg.T * cfg.K
-    gu = costmodel.gate_up(cfg.T, cfg.D, cfg.F, cfg.K, U, cfg.dtype)
-    dn = costmodel.down(cfg.T, cfg.D, cfg.F, cfg.K, U, cfg.dtype, cfg.dtype)
+    ms = statistics.median(step_ms)
+    dts = cfg.dtype
+    gu = costmodel.gate_up(cfg.T, cfg.D, cfg.F, cfg.K, U, dts)
+    dn = costmodel.down(cfg.T, cfg.D, cfg.F, cfg.K, U, dts, dts)
     lay = costmodel.layer(cfg.T, cfg.D, cfg.E, cfg.K, cfg.F, U, cfg.F_shared, cfg.shared_gated,
-                          cfg.dtype, cfg.dtype)
-    st = dict(zip(abi.MOE_STAGE_NAMES, stage_ms))
+                          dts, dts)
+    mfma_peak = (costmodel.MFMA_BF16_PEAK_TFLOPS if dts == "bf16"
+                 else costmodel.MFMA_FP32_PEAK_TFLOPS) * 1e12
+    t_mfma = lay["flops"] / mfma_peak
+    t_hbm = lay["bytes"] / (costmodel.HBM_PEAK_GBS * 1e9)
     res = {
-        "workload": name, "plan": abi.describe_plan(p), "T": cfg.T, "D": cfg.D, "E": cfg.E,
-        "K": cfg.K, "F": cfg.F, "F_shared": cfg.F_shared, "scoring": cfg.scoring, "dtype": cfg.dtype,
-        "ms_per_step": ms_per_step, "gpu_ms_per_step_with_stage_markers": gpu_ms,
-        "tokens_per_s": cfg.T / (ms_per_step / 1e3),
-        "stage_ms": st, "U": U, "assignments": A,
+        "workload": name, "description": cfg.description, "plan": abi.describe_plan(p),
+        "T": cfg.T, "D": cfg.D, "E": cfg.E, "K": cfg.K, "F": cfg.F, "F_shared": cfg.F_shared,
+        "scoring": cfg.scoring, "dtype": dts,
+        "ms_per_step": ms, "ms_per_step_mean": statistics.fmean(step_ms),
+        "ms_per_step_min": min(step_ms), "ms_per_step_max": max(step_ms),
+        "wall_ms_per_step_incl_flush": (t1 - t0) * 1e3 / steps,
+        "tokens_per_s": cfg.T / (ms / 1e3),
+        "U": U, "assignments": cfg.T * cfg.K,
         "t_e": {"min": int(nz.min()), "median": float(nz.median()), "max": int(nz.max())},
-        "layer_tflops": lay["flops"] / (ms_per_step / 1e3) / 1e12,
-        "layer_gbs": lay["bytes"] / (ms_per_step / 1e3) / 1e9,
-        "gate_up": {"ms": gate_up_live_ms, "alg_bytes": gu["bytes"], "alg_flops": gu["flops"],
-                    "gbs": gu["bytes"] / (gate_up_live_ms / 1e3) / 1e9,
-                    "tflops": gu["flops"] / (gate_up_live_ms / 1e3) / 1e12},
-        "down": {"ms": st["down"], "alg_bytes": dn["bytes"], "alg_flops": dn["flops"],
-                 "gbs": dn["bytes"] / (st["down"] / 1e3) / 1e9,
-                 "tflops": dn["flops"] / (st["down"] / 1e3) / 1e12},
+        "layer": {"alg_flops": lay["flops"], "alg_bytes": lay["bytes"],
+                  "tflops": lay["flops"] / (ms / 1e3) / 1e12,
+                  "gbs": lay["bytes"] / (ms / 1e3) / 1e9,
+                  "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+                  "roofline_ms": max(t_mfma, t_hbm) * 1e3,
+                  "roofline_frac": max(t_mfma, t_hbm) / (ms / 1e3)},
+        "gate_up": kernel_roofline(gu["flops"], gu["bytes"], statistics.median(gu_ms),
+                                   mfma_peak / 1e12, costmodel),
+        "down": kernel_roofline(dn["flops"], dn["bytes"], stage_ms["down"], mfma_peak / 1e12,
+                                costmodel),
         "expert_weight_gbs": (gu["weight_bytes"] + dn["weight_bytes"]) /
-                             ((st["gate_up"] + st["down"]) / 1e3) / 1e9,
+                             ((statistics.median(gu_ms) + stage_ms["down"]) / 1e3) / 1e9,
+        "stage_ms": stage_ms,
     }
+    res["expert_weight_hbm_frac"] = res["expert_weight_gbs"] / costmodel.HBM_PEAK_GBS
     return res, layer, cfg
 
 
@@ -206,37 +301,51 @@ def read_traffic(kernel_tag):
         return None
 
 
-def cpu_baseline(cfg, layer, min_seconds):
-    """The float64 oracle, unmodified, on the same batch (host copies), repeated to >= min_seconds."""
-    import numpy as np
+def cpu_baseline(cfg, layer, min_seconds, chunk):
+    """The float64 oracle, unmodified, on consecutive chunks of the same batch (host copies of
+    the tokens; weights upcast expert by expert inside each call, as the oracle does), until at
+    least min_seconds have passed."""
+    import numpy as np  # noqa: F401
     import torch
     from threadpoolctl import threadpool_info
     from oracle import moe_oracle as O
 
-    f32 = lambda t: None if t is None else t.detach().to("cpu", torch.float32).numpy()
-    x = f32(layer["x"])
-    wr = f32(layer["w_router"])
-    wgu = f32(layer["w_gate_up"])
-    wd = f32(layer["w_down"])
-    bias = f32(layer["logit_bias"])
+    class Lazy:
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, e):
+            return self.t[e].detach().to("cpu", torch.float64).numpy()
+
+    f64 = lambda t: None if t is None else t.detach().to("cpu", torch.float64).numpy()
+    wr = f64(layer["w_router"])
+    bias = f64(layer["logit_bias"])
     kw = {}
     if cfg.F_shared:
-        kw = {"ws_gate_up": f32(layer["ws_gate_up"]), "ws_down": f32(layer["ws_down"]),
-              "w_shared_gate": f32(layer["w_shared_gate"])}
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    passes, tokens = 0, 0
+        kw = {"ws_gate_up": f64(layer["ws_gate_up"]), "ws_down": f64(layer["ws_down"]),
+              "w_shared_gate": f64(layer["w_shared_gate"])}
+    info = threadpool_info()
+    blas = [i for i in info if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    vendor = ",".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in blas})) or "?"
+    tokens, calls = 0, 0
     t0 = time.perf_counter()
-    while True:
-        O.moe_forward(x, wr, wgu, wd, cfg.K, cfg.scoring, logit_bias=bias, **kw)
-        passes += 1
-        tokens += cfg.T
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
+    while tokens < cfg.T:
+        n = min(chunk, cfg.T - tokens)
+        x = f64(layer["x"][tokens:tokens + n])
+        O.moe_forward(x, wr, Lazy(layer["w_gate_up"]), Lazy(layer["w_down"]), cfg.K, cfg.scoring,
+                      logit_bias=bias, **kw)
+        tokens += n
+        calls += 1
+        if time.perf_counter() - t0 >= min_seconds:
             break
+    el = time.perf_counter() - t0
     return {"value": tokens / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"full {cfg.T}-token batch of the {cfg.name} layer, {passes} pass(es), "
-                      f"{el:.1f} s, float64 NumPy oracle",
-            "seconds": el}
+            "sample": f"tokens [0, {tokens}) of the {cfg.T}-token {cfg.name} batch in {calls} "
+                      f"oracle call(s) of {chunk} tokens (each upcasts every hit expert's "
+                      f"weights to float64), {el:.1f} s, float64 NumPy oracle",
+            "seconds": el, "blas": vendor, "blas_threads": int(threads),
+            "host_cpus_available": len(os.sched_getaffinity(0))}
 
 
 def main():
@@ -251,94 +360,84 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     hip = HipEvents()
+    if args.workloads == "all":
+        others = [w for w in ALL_WORKLOADS if w != args.workload]
+    elif args.workloads == "none":
+        others = []
+    else:
+        others = [w for w in args.workloads.split(",") if w and w != args.workload]
+
+    peaks = None
+    if not args.no_peaks:
+        peaks = measure_peaks(hip)
+        progress(step="peaks", **{k: v for k, v in peaks.items() if isinstance(v, float)})
+    flush = None
+    if not args.no_flush:
+        flush = (torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda"),
+                 torch.empty(2048, dtype=torch.float32, device="cuda"))
 
     main_res, layer, cfg = run_workload(args.workload, args.steps, args.warmup,
-                                        args.atomic_combine, hip)
-    sys.stderr.write(json.dumps({"progress": "main workload timed",
-                                 "ms_per_step": main_res["ms_per_step"]}) + "\n")
-    decode = None
-    if not args.no_decode:
-        decode, _, _ = run_workload(args.decode_workload, args.steps, args.warmup,
-                                    args.atomic_combine, hip)
-        sys.stderr.write(json.dumps({"progress": "decode workload timed",
-                                     "ms_per_step": decode["ms_per_step"]}) + "\n")
-    mfma_bound = None
-    if not args.no_mfma_workload and args.mfma_workload != args.workload:
-        g, lay, _ = run_workload(args.mfma_workload, args.steps, args.warmup, args.atomic_combine,
-                                 hip)
+                                        args.atomic_combine, flush, hip)
+    progress(step=args.workload, ms_per_step=main_res["ms_per_step"])
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, layer, args.cpu_min_seconds, args.cpu_chunk)
+        progress(step="cpu_baseline", tokens_per_s=cpu["value"])
+    del layer
+    torch.cuda.empty_cache()
+
+    workloads = {args.workload: main_res}
+    for name in others:
+        r, lay, _ = run_workload(name, args.steps, args.warmup, args.atomic_combine, flush, hip)
         del lay
         torch.cuda.empty_cache()
-        pk = costmodel.MFMA_BF16_PEAK_TFLOPS
-        mfma_bound = {
-            "workload": args.mfma_workload, "plan": g["plan"], "T": g["T"], "U": g["U"],
-            "t_e": g["t_e"], "ms_per_step": g["ms_per_step"], "tokens_per_s": g["tokens_per_s"],
-            "gate_up_tflops": g["gate_up"]["tflops"], "gate_up_mfma_frac": g["gate_up"]["tflops"] / pk,
-            "down_tflops": g["down"]["tflops"], "down_mfma_frac": g["down"]["tflops"] / pk,
-            "layer_tflops": g["layer_tflops"], "layer_mfma_frac": g["layer_tflops"] / pk,
-            "stage_ms": g["stage_ms"]}
-        sys.stderr.write(json.dumps({"progress": f"{args.mfma_workload} timed",
-                                     "ms_per_step": g["ms_per_step"]}) + "\n")
-    granularity = None
-    if not args.no_granularity:
-        from mixture_experts_layer_renorm_amd.synth import GRANULARITY_PAIR
-        granularity = {}
-        for name in GRANULARITY_PAIR:
-            g, lay, _ = run_workload(name, args.steps, args.warmup, args.atomic_combine, hip)
-            del lay
-            torch.cuda.empty_cache()
-            granularity[name] = {
-                "T": g["T"], "D": g["D"], "E": g["E"], "K": g["K"], "F": g["F"], "U": g["U"],
-                "plan": g["plan"], "ms_per_step": g["ms_per_step"],
-                "tokens_per_s": g["tokens_per_s"], "layer_tflops": g["layer_tflops"],
-                "gate_up_tflops": g["gate_up"]["tflops"], "down_tflops": g["down"]["tflops"],
-                "gate_up_mfma_frac": g["gate_up"]["tflops"] / costmodel.MFMA_BF16_PEAK_TFLOPS,
-                "stage_ms": g["stage_ms"]}
-            sys.stderr.write(json.dumps({"progress": f"{name} timed",
-                                         "ms_per_step": g["ms_per_step"]}) + "\n")
+        workloads[name] = r
+        progress(step=name, ms_per_step=r["ms_per_step"])
     if args.copy_calibration:
         copy_calibration()
 
     gu = main_res["gate_up"]
-    traffic = read_traffic(f"gate_up_{args.workload}")
     grouped = main_res["plan"].split("grouped gate_up/down: ")[1].split(";")[0]
-    roofline = {"kernel": f"routed gate_up, {grouped} tiles, fused SiLU*up epilogue",
-                "bound": "hbm", "achieved": gu["gbs"], "peak": costmodel.HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": gu["gbs"] / costmodel.HBM_PEAK_GBS, "traffic": traffic,
-                "alg_bytes_per_launch": gu["alg_bytes"], "avg_launch_ms": gu["ms"],
-                "mfma_tflops": gu["tflops"],
-                "mfma_frac": gu["tflops"] / costmodel.MFMA_BF16_PEAK_TFLOPS}
+    if gu["bound"] == "mfma":
+        achieved, peak, unit = gu["tflops"], costmodel.MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        measured_peak = peaks["mfma_bf16_tflops"] if peaks else None
+    else:
+        achieved, peak, unit = gu["gbs"], costmodel.HBM_PEAK_GBS, "GB/s"
+        measured_peak = peaks["hbm_read_gbs"] if peaks else None
+    roofline = {"kernel": f"routed gate_up ({grouped} tiles, fused SiLU*up epilogue)",
+                "bound": gu["bound"], "achieved": achieved, "peak": peak, "unit": unit,
+                "frac": achieved / peak, "traffic": read_traffic(f"gate_up_{args.workload}"),
+                "alg_flops_per_launch": gu["alg_flops"], "alg_bytes_per_launch": gu["alg_bytes"],
+                "avg_launch_ms": gu["ms"], "launch_ms_statistic": "median of per-step events",
+                "measured_peak": measured_peak,
+                "frac_of_measured_peak": achieved / measured_peak if measured_peak else None}
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, layer, args.cpu_min_seconds)
-    del layer
-    torch.cuda.empty_cache()
-
+    summary = {n: {"ms_per_step": r["ms_per_step"], "tokens_per_s": r["tokens_per_s"],
+                   "layer_bound": r["layer"]["bound"],
+                   "layer_roofline_frac": r["layer"]["roofline_frac"],
+                   "gate_up_bound": r["gate_up"]["bound"], "gate_up_frac": r["gate_up"]["frac"],
+                   "gate_up_tflops": r["gate_up"]["tflops"], "gate_up_gbs": r["gate_up"]["gbs"],
+                   "expert_weight_hbm_frac": r["expert_weight_hbm_frac"]}
+               for n, r in workloads.items()}
     line = {
         "metric": "MoE-layer tokens/s; grouped-GEMM TFLOP/s (% MFMA peak); decode HBM GB/s",
         "value": main_res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0, std) inputs and random-init weights of the layer's shapes)",
         "config": {"workload": f"{args.workload}: {cfg.description}", "T": cfg.T, "D": cfg.D,
-                   "E": cfg.E, "K": cfg.K, "F": cfg.F, "combine":
-                   "fused fp32 atomics" if args.atomic_combine else "gather (deterministic)"},
+                   "E": cfg.E, "K": cfg.K, "F": cfg.F, "F_shared": cfg.F_shared,
+                   "scoring": cfg.scoring,
+                   "combine": "fused fp32 atomics" if args.atomic_combine
+                   else "gather (deterministic)",
+                   "flush_between_steps": None if args.no_flush else "1 GiB read"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "grouped_gemm": {"gate_up_tflops": gu["tflops"],
-                         "gate_up_mfma_frac": gu["tflops"] / costmodel.MFMA_BF16_PEAK_TFLOPS,
-                         "down_tflops": main_res["down"]["tflops"],
-                         "down_mfma_frac": main_res["down"]["tflops"] /
-                                           costmodel.MFMA_BF16_PEAK_TFLOPS},
-        "main": main_res,
-        "decode": None if decode is None else {
-            "workload": args.decode_workload, "tokens_per_s": decode["tokens_per_s"],
-            "ms_per_step": decode["ms_per_step"], "U": decode["U"],
-            "expert_weight_gbs": decode["expert_weight_gbs"],
-            "expert_weight_hbm_frac": decode["expert_weight_gbs"] / costmodel.HBM_PEAK_GBS,
-            "stage_ms": decode["stage_ms"]},
-        "mfma_bound": mfma_bound,
-        "granularity": granularity,
+        "peaks": {"spec_hbm_gbs": costmodel.HBM_PEAK_GBS,
+                  "spec_mfma_bf16_tflops": costmodel.MFMA_BF16_PEAK_TFLOPS,
+                  "measured": peaks},
+        "summary": summary,
+        "workloads": workloads,
     }
     print(json.dumps(line))
 

@@ -24,11 +24,12 @@
 extern "C" {
 #endif
 
-/* Reads `bytes` bytes of `buf` once with 16-byte vector loads (2048 work-groups of 4 waves,
- * eight loads in flight per lane) and folds them into sink[0..2047] (the loaded bits
- * XOR-combined per work-group, so the loads cannot be removed).  bytes must be a positive
- * multiple of 64 KiB; buf and sink 16-byte aligned; sink holds 2048 floats.  Time it with
- * events: bytes / duration is the achieved read rate. */
+/* Reads `bytes` bytes of `buf` once with 16-byte vector loads: up to 8192 work-groups of 8
+ * waves, each sweeping one contiguous chunk with four loads in flight per lane.  sink (2048
+ * floats) is written only if a work-group's loaded words XOR to a fixed value; it keeps the
+ * loads from being removed.  bytes must be a positive multiple of 64 KiB; buf and sink 16-byte
+ * aligned.  Time it with events: bytes / duration is the achieved read rate.  A read of 1 GiB
+ * also evicts the L2s and the 256 MiB MALL without leaving dirty lines behind. */
 int moe_peak_hbm_read(const void *buf, size_t bytes, float *sink, moe_stream_t stream);
 
 /* Runs `iters` rounds of 8 independent v_mfma_f32_16x16x32_bf16 per wave on register

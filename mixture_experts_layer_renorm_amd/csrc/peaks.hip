@@ -8,37 +8,29 @@
 namespace moe {
 namespace {
 
-constexpr int kReadGroups = 2048;
-constexpr int kReadThreads = 256;
-constexpr int kReadDepth = 8;  // 16-byte loads in flight per lane
+constexpr int kReadGroups = 8192;
+constexpr int kReadThreads = 512;
+constexpr int kReadDepth = 4;  // 16-byte loads in flight per lane
 
+// Each work-group sweeps one contiguous chunk of the buffer (the fastest of the read patterns
+// measured on MI355X: a grid-stride sweep reaches about 10% less).  The sink is written only
+// if a work-group's loaded words XOR to a fixed value, which keeps every load alive.
 __global__ void __launch_bounds__(kReadThreads) hbm_read_kernel(const uint4* __restrict__ buf,
                                                                 int64_t n16,
                                                                 float* __restrict__ sink) {
-  __shared__ uint32_t part[kReadThreads / 64];
-  const int64_t stride = (int64_t)kReadGroups * kReadThreads;
-  int64_t i = (int64_t)blockIdx.x * kReadThreads + threadIdx.x;
+  const int64_t chunk = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * chunk;
+  const int64_t hi = lo + chunk < n16 ? lo + chunk : n16;
   uint32_t acc = 0;
-  for (; i + (kReadDepth - 1) * stride < n16; i += kReadDepth * stride) {
+  for (int64_t i = lo + threadIdx.x; i < hi; i += (int64_t)kReadDepth * kReadThreads) {
     uint4 v[kReadDepth];
 #pragma unroll
-    for (int k = 0; k < kReadDepth; ++k) v[k] = buf[i + k * stride];
+    for (int k = 0; k < kReadDepth; ++k)
+      v[k] = i + k * kReadThreads < hi ? buf[i + k * kReadThreads] : uint4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < kReadDepth; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
   }
-  for (; i < n16; i += stride) {
-    const uint4 v = buf[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m, 64);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = 0;
-    for (int w = 0; w < kReadThreads / 64; ++w) r ^= part[w];
-    sink[blockIdx.x] = __uint_as_float(r);
-  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x & 2047] = 1.0f;
 }
 
 __global__ void __launch_bounds__(256) mfma_loop_kernel(int iters, float* __restrict__ sink) {
@@ -73,7 +65,10 @@ int moe_peak_hbm_read(const void* buf, size_t bytes, float* sink, moe_stream_t s
   if (!buf || !sink || (reinterpret_cast<uintptr_t>(buf) & 15) ||
       (reinterpret_cast<uintptr_t>(sink) & 15) || bytes == 0 || bytes % 65536)
     return MOE_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(moe::hbm_read_kernel, dim3(moe::kReadGroups), dim3(moe::kReadThreads), 0,
+  // at least 64 KiB per work-group
+  const size_t groups = bytes / 65536 < (size_t)moe::kReadGroups ? bytes / 65536
+                                                                  : (size_t)moe::kReadGroups;
+  hipLaunchKernelGGL(moe::hbm_read_kernel, dim3((unsigned)groups), dim3(moe::kReadThreads), 0,
                      (hipStream_t)stream, (const uint4*)buf, (int64_t)(bytes / 16), sink);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
