@@ -251,6 +251,21 @@ int moe_forward_timed(const moe_problem *p, const void *x, const moe_weights *w,
                       moe_routing *r_opt, void *out, void *workspace, size_t workspace_bytes,
                       moe_stream_t stream, void *const *events);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): moe_forward without a workspace argument.  Its
+ * kernels use a fixed scratch array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends; the caller still passes inputs and outputs.
+ * Same results and errors as moe_forward with a workspace, plus MOE_ERR_WORKSPACE (nothing
+ * enqueued) when moe_workspace_size(p) exceeds the scratch size -- e.g. bf16 35B-A3B-shaped
+ * batches (D=2048, E=256, K=8, F=512) fit up to a few hundred tokens.  The first call on a
+ * device looks up that device's scratch address (no allocation).  Every call on one GPU shares
+ * its scratch, which keeps the last call's contents (nothing in it needs to start at zero):
+ * calls that may overlap on one GPU -- different streams, or several host threads -- race and
+ * must be serialised by the caller.  Never allocates, frees or synchronises. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const moe_problem *p, const void *x, const moe_weights *w,
+                        moe_routing *r_opt, void *out, moe_stream_t stream);
+
 /* Static text for a status code. */
 const char *moe_status_string(int status);
 

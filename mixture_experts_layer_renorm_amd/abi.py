@@ -44,7 +44,9 @@ DISPATCH_KERNELS = {"auto": MOE_DISPATCH_AUTO, "one_workgroup": MOE_DISPATCH_ONE
 SYMBOLS = ("moe_workspace_size", "moe_route", "moe_route_logits", "moe_dispatch",
            "moe_experts", "moe_combine", "moe_forward", "moe_forward_timed",
            "moe_status_string", "moe_last_error", "moe_describe_plan", "moe_update_select_bias",
-           "moe_router_stats", "moe_peak_hbm_read", "moe_peak_mfma_bf16")
+           "moe_router_stats", "moe_peak_hbm_read", "moe_peak_mfma_bf16",
+           "moe_forward_noalloc")
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_STAGE_NAMES = ("router", "topk", "dispatch", "gate_up", "shared", "down", "final")
 MOE_STAGE_COUNT = len(MOE_STAGE_NAMES)
 MOE_STAGE_GATE_UP = MOE_STAGE_NAMES.index("gate_up")
@@ -109,9 +111,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward.argtypes = [prob, vp, P(moe_weights), P(moe_routing), vp, vp, sz, vp]
     lib.moe_forward_timed.argtypes = [prob, vp, P(moe_weights), P(moe_routing), vp, vp, sz, vp,
                                       P(ctypes.c_void_p)]
+    lib.moe_forward_noalloc.argtypes = [prob, vp, P(moe_weights), P(moe_routing), vp, vp]
     for n in ("moe_workspace_size", "moe_route", "moe_route_logits", "moe_dispatch",
               "moe_experts", "moe_combine", "moe_forward", "moe_forward_timed",
-              "moe_update_select_bias", "moe_router_stats"):
+              "moe_update_select_bias", "moe_router_stats", "moe_forward_noalloc"):
         getattr(lib, n).restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -312,6 +315,17 @@ def moe_forward(p: moe_problem, x: torch.Tensor, weights: Dict, routing: Optiona
                            ctypes.byref(r) if r is not None else None,
                            _ptr(out, "out", _DTYPE_OF_CODE[p.out_dtype]), wp, wb,
                            _stream(stream)))
+
+
+def moe_forward_noalloc(p: moe_problem, x: torch.Tensor, weights: Dict, routing: Optional[Dict],
+                        out: torch.Tensor, stream=None) -> None:
+    """moe_forward on the library's fixed per-GPU scratch: no workspace, no allocation."""
+    lib = load_library()
+    w, r = _weights(p, weights), _routing(routing)
+    _check(lib.moe_forward_noalloc(ctypes.byref(p), _ptr(x, "x", problem_dtype(p)),
+                                   ctypes.byref(w), ctypes.byref(r) if r is not None else None,
+                                   _ptr(out, "out", _DTYPE_OF_CODE[p.out_dtype]),
+                                   _stream(stream)))
 
 
 def moe_forward_timed(p: moe_problem, x: torch.Tensor, weights: Dict, routing: Optional[Dict],

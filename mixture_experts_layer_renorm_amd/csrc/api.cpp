@@ -8,6 +8,7 @@
 #include <cstdlib>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe.h"
@@ -769,9 +770,52 @@ int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_
   return MOE_OK;
 }
 
+// Scratch of moe_forward_noalloc: one copy per GPU (a device global lives in each device's
+// copy of the code object).  In host code `scratch` names a host-side stand-in, not device
+// memory, so it is never passed to a kernel or a copy: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  MOE_HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    MOE_HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int moe_forward_noalloc(const moe_problem* p, const void* x, const moe_weights* w,
+                        moe_routing* r_opt, void* out, moe_stream_t stream) {
+  g_last_error.clear();
+  int st = check_problem(p);
+  if (st) return st;
+  if (p->T == 0) return MOE_OK;
+  const size_t need = layout(p).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "problem needs %zu bytes of workspace, more than the %zu-byte scratch of "
+                "moe_forward_noalloc (use moe_forward with a workspace)",
+                need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return forward_impl(p, x, w, r_opt, out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+}
 
 int moe_forward(const moe_problem* p, const void* x, const moe_weights* w, moe_routing* r_opt,
                 void* out, void* workspace, size_t workspace_bytes, moe_stream_t stream) {

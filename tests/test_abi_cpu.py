@@ -251,6 +251,26 @@ def test_invalid_calls_fail_before_launch(lib):
                            None) == abi.MOE_ERR_INVALID_ARG
 
 
+def test_noalloc_rejects_before_touching_the_device(lib):
+    """moe_forward_noalloc validates the problem and its workspace need against the fixed
+    scratch size before it looks up any device."""
+    import torch
+    w = _weights()
+    out = ALIGNED
+    big = abi.make_problem(T=4096, D=2048, E=256, K=8, F=512, dtype=torch.bfloat16)
+    st, need = _ws_size(lib, big)
+    assert st == abi.MOE_OK and need > abi.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(ctypes.byref(big), ALIGNED + 4096, ctypes.byref(w), None, out,
+                                   None) == abi.MOE_ERR_WORKSPACE
+    assert b"scratch" in lib.moe_last_error()
+    small = abi.make_problem(T=64, D=2048, E=256, K=8, F=512, dtype=torch.bfloat16)
+    assert _ws_size(lib, small)[1] <= abi.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(ctypes.byref(_prob(K=9)), ALIGNED, ctypes.byref(w), None, out,
+                                   None) == abi.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_noalloc(ctypes.byref(_prob(T=0)), None, None, None, None,
+                                   None) == abi.MOE_OK
+
+
 def test_empty_batch_returns_ok_without_touching_pointers(lib):
     p = _prob(T=0)
     w = abi.moe_weights()
