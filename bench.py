@@ -125,7 +125,7 @@ def measure_peaks(hip, reps=5):
     buf.fill_(1)
     sink = torch.empty(65536, dtype=torch.float32, device="cuda")
     waves, iters = 2048, 40000  # 8 waves per CU; 10.7 TFLOP per launch (about 5 ms)
-    mfma_flops = waves * iters * 8 * 16384
+    mfma_flops = waves * iters * 4 * 32768
     res = {}
     for name, launch, work in (
             ("hbm_read", lambda: abi.moe_peak_hbm_read(buf, sink), nbytes),
@@ -149,7 +149,7 @@ def measure_peaks(hip, reps=5):
     return {"hbm_read_gbs": res["hbm_read"][1] / 1e9, "hbm_read_bytes": nbytes,
             "hbm_read_ms": res["hbm_read"][0],
             "mfma_bf16_tflops": res["mfma_bf16"][1] / 1e12, "mfma_bf16_ms": res["mfma_bf16"][0],
-            "mfma_loop": f"{waves} waves x {iters} x 8 v_mfma_f32_16x16x32_bf16 on registers"}
+            "mfma_loop": f"{waves} waves x {iters} x 4 v_mfma_f32_32x32x16_bf16 on registers"}
 
 
 def kernel_roofline(flops, nbytes, ms, mfma_peak_tflops, costmodel):

@@ -32,9 +32,9 @@ extern "C" {
  * also evicts the L2s and the 256 MiB MALL without leaving dirty lines behind. */
 int moe_peak_hbm_read(const void *buf, size_t bytes, float *sink, moe_stream_t stream);
 
-/* Runs `iters` rounds of 8 independent v_mfma_f32_16x16x32_bf16 per wave on register
+/* Runs `iters` rounds of 4 independent v_mfma_f32_32x32x16_bf16 per wave on register
  * operands, on `waves` waves (64 lanes each; a multiple of 4, at most 65536), and writes one
- * float per wave to sink[0..waves-1].  FLOPs executed: waves * iters * 8 * 16384. */
+ * float per wave to sink[0..waves-1].  FLOPs executed: waves * iters * 4 * 32768. */
 int moe_peak_mfma_bf16(int waves, int iters, float *sink, moe_stream_t stream);
 
 #ifdef __cplusplus

@@ -356,7 +356,7 @@ def moe_peak_hbm_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> Non
 
 
 def moe_peak_mfma_bf16(waves: int, iters: int, sink: torch.Tensor, stream=None) -> None:
-    """waves * iters * 8 bf16 MFMAs of 16x16x32 on registers; sink: >= waves fp32."""
+    """waves * iters * 4 bf16 MFMAs of 32x32x16 on registers; sink: >= waves fp32."""
     lib = load_library()
     if sink.numel() < waves:
         raise ValueError("sink must hold one float per wave")
