@@ -71,6 +71,11 @@ def parse_args():
     ap.add_argument("--no-flush", action="store_true",
                     help="do not read 1 GiB between steps (weights may stay in the MALL)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured machine peaks")
+    ap.add_argument("--gemm-kernel", default="auto", choices=("auto", "tile32", "tile256", "mfma"),
+                    help="force the grouped GEMM (moe_problem.gemm_kernel), for tuning")
+    ap.add_argument("--dispatch-kernel", default="auto",
+                    choices=("auto", "one_workgroup", "multi"),
+                    help="force the dispatch kernel (moe_problem.dispatch_kernel), for tuning")
     ap.add_argument("--atomic-combine", action="store_true",
                     help="time the fused fp32-atomic combine instead of the default gather")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -165,7 +170,8 @@ def kernel_roofline(flops, nbytes, ms, mfma_peak_tflops, costmodel):
             "bound": bound, "frac": frac, "mfma_peak_tflops": mfma_peak_tflops}
 
 
-def run_workload(name, steps, warmup, atomic_combine, flush, hip):
+def run_workload(name, steps, warmup, atomic_combine, flush, hip, gemm_kernel="auto",
+                 dispatch_kernel="auto"):
     import torch
     from mixture_experts_layer_renorm_amd import abi, costmodel
     from mixture_experts_layer_renorm_amd.synth import CONFIGS, make_layer
@@ -175,7 +181,8 @@ def run_workload(name, steps, warmup, atomic_combine, flush, hip):
     layer = make_layer(cfg, device=dev, seed=0)
     p = abi.make_problem(T=cfg.T, D=cfg.D, E=cfg.E, K=cfg.K, F=cfg.F, F_shared=cfg.F_shared,
                          shared_gated=cfg.shared_gated, scoring=cfg.scoring, dtype=cfg.torch_dtype,
-                         atomic_combine=atomic_combine)
+                         atomic_combine=atomic_combine, gemm_kernel=gemm_kernel,
+                         dispatch_kernel=dispatch_kernel)
     weights = {"w_router": layer["w_router"], "logit_bias": layer["logit_bias"],
                "w_gate_up": layer["w_gate_up"], "w_down": layer["w_down"],
                "ws_gate_up": layer["ws_gate_up"], "ws_down": layer["ws_down"],
@@ -377,7 +384,8 @@ def main():
                  torch.empty(2048, dtype=torch.float32, device="cuda"))
 
     main_res, layer, cfg = run_workload(args.workload, args.steps, args.warmup,
-                                        args.atomic_combine, flush, hip)
+                                        args.atomic_combine, flush, hip, args.gemm_kernel,
+                                        args.dispatch_kernel)
     progress(step=args.workload, ms_per_step=main_res["ms_per_step"])
     cpu = None
     if not args.no_cpu_baseline:
@@ -388,7 +396,8 @@ def main():
 
     workloads = {args.workload: main_res}
     for name in others:
-        r, lay, _ = run_workload(name, args.steps, args.warmup, args.atomic_combine, flush, hip)
+        r, lay, _ = run_workload(name, args.steps, args.warmup, args.atomic_combine, flush, hip,
+                                 args.gemm_kernel, args.dispatch_kernel)
         del lay
         torch.cuda.empty_cache()
         workloads[name] = r

@@ -133,20 +133,50 @@ moe::TileCfg grouped_cfg(const moe_problem* p) {
   return mean <= 48 ? moe::TILE_SMALL : moe::TILE_LARGE;
 }
 
-// Router: bf16 batches of up to 1024 tokens use the split-K matrix-core router (partial sums
-// reduced by the top-K kernel), which keeps the latency of a short batch low; larger batches
-// and fp32 layers use the tile GEMM (one slice).
-bool router_split(const moe_problem* p) { return p->dtype == MOE_DTYPE_BF16 && p->T <= 1024; }
-int router_ks(const moe_problem* p) {
-  return router_split(p) ? moe::router_kslices(p->T, p->D, p->E, gated(p) ? 1 : 0) : 1;
-}
-
 // Dense GEMMs: large tiles unless they would leave CUs idle.  The router (extra gate column,
 // column bias) stays on the tile GEMM.
 moe::TileCfg dense_cfg(int64_t M, int64_t N) {
   const int64_t bm = moe::tile_bm(moe::TILE_LARGE), bn = moe::tile_bn(moe::TILE_LARGE);
   const bool big = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) >= moe::kCus;
   return big ? moe::TILE_LARGE : moe::TILE_SMALL;
+}
+
+// Router: bf16 batches of up to 1024 tokens use the split-K matrix-core router (partial sums
+// reduced by the top-K kernel), which keeps the latency of a short batch low.  Larger bf16
+// batches use the tile GEMM, whose speed here is set by the bytes its DMA rings keep in flight
+// per CU: 32 x 128 tiles with the reduction split (up to 8 slices of at least 8 K steps, summed
+// in order by the top-K kernel) until two work-groups per CU run; when the 32-row tiles alone
+// exceed that, 256 x 128 tiles (a quarter of the re-reads of the router weights) split until
+// they fill every CU, if they can.  fp32 layers use the tile GEMM unsplit.
+bool router_split(const moe_problem* p) { return p->dtype == MOE_DTYPE_BF16 && p->T <= 1024; }
+
+struct RouterTiles {
+  moe::TileCfg cfg;
+  int ks;
+};
+
+RouterTiles router_tiles(const moe_problem* p) {
+  const int64_t ncols = p->E + (gated(p) ? 1 : 0);
+  if (p->dtype != MOE_DTYPE_BF16) return {dense_cfg(p->T, ncols), 1};
+  const int nk = p->D / 64;  // 64-wide K steps of bf16 rows
+  const auto split = [&](int64_t tiles, int64_t slots) {
+    int ks = 1;
+    while (ks * 2 <= 8 && tiles * ks * 2 <= slots && nk % (ks * 2) == 0 && nk / (ks * 2) >= 8)
+      ks *= 2;
+    return ks;
+  };
+  const int64_t nt = (ncols + 127) / 128;
+  const int64_t small = (p->T + 31) / 32 * nt, large = (p->T + 255) / 256 * nt;
+  const int64_t slots = 2 * moe::kCus;  // 32-row tiles: two work-groups per CU
+  if (small < slots) return {moe::TILE_SMALL, split(small, slots)};
+  const int ks = split(large, moe::kCus);
+  if (large * ks >= moe::kCus) return {moe::TILE_LARGE, ks};
+  return {moe::TILE_SMALL, 1};
+}
+
+int router_ks(const moe_problem* p) {
+  return router_split(p) ? moe::router_kslices(p->T, p->D, p->E, gated(p) ? 1 : 0)
+                         : router_tiles(p).ks;
 }
 
 // The shared expert's two GEMMs: the matrix-core GEMM (dense 256 x 256 tiles) for bf16
@@ -177,12 +207,13 @@ Layout layout(const moe_problem* p) {
     return at;
   };
   L.max_mtiles = (A + 31) / 32 + (E < A ? E : A);  // upper bound for the smallest BM (32)
-  {  // router output: logits [T, E], or the split-K partial sums [ks][T][E + gated]
+  {  // router output: the split-K partial sums [ks][T][E + gated] (small batches) or
+     // [ks][T][E] (tile GEMM; the gate logit's partials [ks][T] go to gate_logit)
     const size_t ks = (size_t)router_ks(p);
-    const size_t a = (size_t)T * E * 4, b = ks * (size_t)T * (E + (gated(p) ? 1 : 0)) * 4;
-    L.logits = take(a > b ? a : b);
+    const size_t b = ks * (size_t)T * (E + (gated(p) ? 1 : 0)) * 4;
+    L.logits = take(b);
+    L.gate_logit = take(ks * (size_t)T * 4);
   }
-  L.gate_logit = take((size_t)T * 4);
   L.gate = take((size_t)T * 4);
   L.topk_idx = take((size_t)A * 4);
   L.topk_w = take((size_t)A * 4);
@@ -257,6 +288,7 @@ hipError_t run_router(const moe_problem* p, const void* x, const moe_weights* w,
     ta->slice_stride = p->T * ne;
     ta->gate_src = gate_w ? part + p->E : nullptr;
     ta->gate_ld = ne;
+    ta->gate_slice_stride = p->T * ne;
     return moe::launch_router_bf16(x, w->w_router, gate_w, w->logit_bias, p->T, p->D, p->E, ks,
                                    part, s);
   }
@@ -274,14 +306,18 @@ hipError_t run_router(const moe_problem* p, const void* x, const moe_weights* w,
   g.ldc = p->E;
   g.C2 = gate_w ? gate_logit : nullptr;
   g.col_bias = w->logit_bias;
-  ta->ks = 1;
+  const RouterTiles rt = router_tiles(p);
+  g.k_slices = rt.ks;
+  g.c_slice_stride = p->T * p->E;
+  g.c2_slice_stride = p->T;
+  ta->ks = rt.ks;
   ta->ld = p->E;
-  ta->slice_stride = 0;
+  ta->slice_stride = p->T * p->E;
   ta->gate_src = gate_w ? gate_logit : nullptr;
   ta->gate_ld = 1;
-  const moe::TileCfg cfg = dense_cfg(p->T, p->E + (gate_w ? 1 : 0));
-  const int bm = moe::tile_bm(cfg);
-  return moe::launch_gemm(p->dtype, cfg, moe::EPI_STORE, g, (p->T + bm - 1) / bm, s);
+  ta->gate_slice_stride = p->T;
+  const int bm = moe::tile_bm(rt.cfg);
+  return moe::launch_gemm(p->dtype, rt.cfg, moe::EPI_STORE, g, (p->T + bm - 1) / bm, s);
 }
 
 // A grouped GEMM over the tile map.
@@ -433,7 +469,7 @@ const char* moe_describe_plan(const moe_problem* p) {
   const std::string router =
       router_split(p)
           ? "split-K mfma 16x64, " + std::to_string(router_ks(p)) + " K slice(s)"
-          : name(dense_cfg(p->T, p->E + (gated(p) ? 1 : 0)));
+          : name(router_tiles(p).cfg) + ", " + std::to_string(router_tiles(p).ks) + " K slice(s)";
   text = "router: " + router + "; dispatch: " +
          (moe::dispatch_fused(p->T * p->K, p->E, p->dispatch_kernel) ? "one work-group"
                                                                       : "count, then scan+scatter") +

@@ -103,10 +103,12 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
   constexpr int BNE = kSwiglu ? BN / 2 : BN;  // output columns per tile
   const int ntN = (ncols + BNE - 1) / BNE;
   const int mt_total = p.tiles ? load_uniform(p.tile_count, 0) : (p.M + BM - 1) / BM;
-  const int nt = mt_total * ntN;
+  // split-K (dense STORE only): logical tile t is reduction slice t % ks of output tile t / ks
+  const int ks = (EPI == EPI_STORE && !p.tiles && p.k_slices > 1) ? p.k_slices : 1;
+  const int nt = mt_total * ntN * ks;
   const int xcd = blockIdx.x % kXcds, per = gridDim.x / kXcds, jb = blockIdx.x / kXcds;
   const int lo = (int)((int64_t)nt * xcd / kXcds), hi = (int)((int64_t)nt * (xcd + 1) / kXcds);
-  const int nk = p.Kdim / KE;
+  const int nk = p.Kdim / KE / ks;  // K steps per slice (the host makes ks divide them)
 
   // LDS rows of this wave's B sub-tiles (SwiGLU: gate j and up j sit NI/2 sub-tiles apart).
   int blds[NI];
@@ -120,8 +122,10 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
     }
   }
 
-  for (int t = lo + jb; t < hi; t += per) {
+  for (int tk = lo + jb; tk < hi; tk += per) {
     // ---- decode the logical tile: expert-major, then N tile, then M tile -------------------
+    const int kslice = tk % ks, t = tk / ks;
+    const int64_t k0 = (int64_t)kslice * nk * kRowBytes;  // this slice's first byte of a row
     const int q = t / ntN;
     int first, cnt;
     if (p.tiles) {
@@ -187,19 +191,19 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
 
 #pragma unroll
     for (int st = 0; st < S - 1; ++st)
-      if (st < nk) dma_step<L>(src, (int64_t)st * kRowBytes, smem[st], wave);
+      if (st < nk) dma_step<L>(src, k0 + (int64_t)st * kRowBytes, smem[st], wave);
 
-    for (int ks = 0; ks < nk; ++ks) {
-      // this wave's DMA for step ks has landed (later steps may still fly), earlier LDS reads
-      // are complete; the barrier then publishes step ks and frees stage (ks - 1) % S
-      if (ks + S - 2 < nk)
+    for (int kk = 0; kk < nk; ++kk) {
+      // this wave's DMA for step kk has landed (later steps may still fly), earlier LDS reads
+      // are complete; the barrier then publishes step kk and frees stage (kk - 1) % S
+      if (kk + S - 2 < nk)
         barrier_after<L * (S - 2), 0>();
       else
         barrier_after<0, 0>();
-      if (ks + S - 1 < nk)
-        dma_step<L>(src, (int64_t)(ks + S - 1) * kRowBytes, smem[(ks + S - 1) % S], wave);
+      if (kk + S - 1 < nk)
+        dma_step<L>(src, k0 + (int64_t)(kk + S - 1) * kRowBytes, smem[(kk + S - 1) % S], wave);
 
-      const char* sm = smem[ks % S];
+      const char* sm = smem[kk % S];
       if constexpr (!kF32) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -268,7 +272,9 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
         }
       }
     } else if constexpr (EPI == EPI_STORE) {
-      float* C = (float*)p.C;
+      float* C = (float*)p.C + kslice * p.c_slice_stride;
+      float* C2 = p.C2 ? p.C2 + kslice * p.c2_slice_stride : nullptr;
+      const float* col_bias = kslice == 0 ? p.col_bias : nullptr;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -282,10 +288,10 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
             const int n = n_tile * BN + wn * WTN + j * 16 + lr;
             const float v = acc[i][j][r];
             if (n < p.N) {
-              const float b = p.col_bias ? p.col_bias[n] : 0.0f;
+              const float b = col_bias ? col_bias[n] : 0.0f;
               C[grow * p.ldc + n] = (v + b) * scale;
             } else if (p.B2 && n == p.N) {
-              p.C2[grow] = v;
+              C2[grow] = v;
             }
           }
         }
@@ -317,7 +323,9 @@ hipError_t launch_cfg(Epilogue epi, const GemmParams& p, int64_t max_mtiles, int
   const int ncols = epi == EPI_SWIGLU ? p.N : p.N + (p.B2 ? 1 : 0);
   const int bne = epi == EPI_SWIGLU ? BN / 2 : BN;
   const int64_t ntN = (ncols + bne - 1) / bne;
-  int64_t want = max_mtiles * ntN;
+  const int ks = (epi == EPI_STORE && !p.tiles && p.k_slices > 1) ? p.k_slices : 1;
+  if (ks > 1 && (p.Kdim / (kRowBytes / (int)sizeof(T))) % ks != 0) return hipErrorInvalidValue;
+  int64_t want = max_mtiles * ntN * ks;
   int64_t cap = (int64_t)kCus * occupancy;
   int64_t grid = want < cap ? want : cap;
   grid = ((grid + kXcds - 1) / kXcds) * kXcds;

@@ -58,6 +58,11 @@ struct GemmParams {
   int64_t ldcs;
   float* C2;                // STORE: column N (if B2) -> C2[row]
   const float* col_bias;    // STORE: + col_bias[n]
+  int32_t k_slices;         // tile GEMM, dense STORE: split the reduction into this many
+                            // equal slices (<= 1: none); slice z writes its partial sums to
+                            // C + z * c_slice_stride and C2 + z * c2_slice_stride (col_bias
+                            // in slice 0 only)
+  int64_t c_slice_stride, c2_slice_stride;
   const float* row_scale;   // STORE: * row_scale[row]
   float* acc_out;           // ATOMIC: [tokens, ldo]
   int64_t ldo;
@@ -87,7 +92,7 @@ hipError_t launch_gemm(int dtype, TileCfg cfg, Epilogue epi, const GemmParams& p
 // t * ld + e] over q < ks (ks = 1: src is the logits matrix).  Writes idx/w [T, K]; optionally
 // the summed logits [T, E] to logits_out, the selection keys [T, E] (the logit, or with
 // sel_bias the fp32 score + bias) to keys_out, and sigmoid of the gate logit (same summation
-// over gate_src[q * slice_stride + t * gate_ld]) to gate_out [T].
+// over gate_src[q * gate_slice_stride + t * gate_ld]) to gate_out [T].
 struct TopkArgs {
   const float* src;
   int ks;
@@ -101,6 +106,7 @@ struct TopkArgs {
   float* keys_out;
   const float* gate_src;
   int64_t gate_ld;
+  int64_t gate_slice_stride;
   float* gate_out;
   const float* sel_bias;  // [E] or null: choose on score + bias, weight with the score
 };

@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const TopkArgs a) {
   }
   if (a.gate_out && lane == 0) {
     float g = a.gate_src[t * a.gate_ld];
-    for (int q = 1; q < a.ks; ++q) g += a.gate_src[q * a.slice_stride + t * a.gate_ld];
+    for (int q = 1; q < a.ks; ++q) g += a.gate_src[q * a.gate_slice_stride + t * a.gate_ld];
     a.gate_out[t] = 1.0f / (1.0f + expf(-g));
   }
 }

@@ -97,11 +97,14 @@ def _fp32_logit_bound(X, W, logits64):
 
 # bf16 batches of up to 1024 tokens take the split-K router (K slices summed by the top-K
 # kernel: 8 slices at T=64, 4 for the gated 513-column a17b router at T=70, 1 past 256 blocks);
-# larger batches and fp32 take the tile GEMM.
+# larger bf16 batches take the tile GEMM with its reduction split into up to 8 slices (4 at
+# T=1025 with a ragged last M tile, 2 for the gated 513-column a17b router at T=1100 and at
+# T=3000 of the sigmoid layer, 1 at T=2000 of a17b), fp32 the unsplit tile GEMM.
 @pytest.mark.parametrize("name,T", [("tiny", 64), ("a3b_prefill", 333), ("a17b", 70),
                                     ("skew", 200), ("ds_sigmoid", 90), ("a3b_decode", 64),
                                     ("a3b_prefill", 1), ("a17b", 1), ("a3b_prefill", 1024),
-                                    ("a3b_prefill", 1025)])
+                                    ("a3b_prefill", 1025), ("a17b", 1100), ("a17b", 2000),
+                                    ("skew", 4096), ("ds_sigmoid", 3000)])
 def test_router_gemm_and_topk(name, T):
     cfg = CONFIGS[name]
     # only the router's tensors, drawn on the CPU at the workload's real widths
