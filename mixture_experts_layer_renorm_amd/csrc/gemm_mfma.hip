@@ -21,6 +21,7 @@
 //  * LDS rows are 128 bytes; the eight 16-byte chunks of row r are XOR-swizzled by
 //    (r >> 1) & 7, which keeps the 16-row operand fetches conflict-free.
 //  * Token rows are gathered through the dispatch permutation by the DMA addresses themselves.
+//    Weight DMAs are non-temporal (see kWeightAux).
 //  * Persistent, XCD-aware schedule over logical tiles ordered expert-major, then N tile, then
 //    M tile, so the tiles that share an expert's weights or rows meet in one XCD's L2.  With
 //    three or more K stages the rings run on across a work-group's tiles: a tile's last
@@ -86,13 +87,13 @@ __device__ __forceinline__ void lds_barrier() {
 // One stage of one operand (up to 256 rows x 128 bytes) by one of NW waves: instruction i fills
 // staged rows [8 (wave + NW i), +8), so the first N instructions of the 8 waves fill rows
 // [0, 64 N); src holds the lane's 32-bit byte offsets from base.
-template <int NW, int N = kBM / 8 / NW>
+template <int NW, int N = kBM / 8 / NW, int AUX = 0>
 __device__ __forceinline__ void dma_operand(const char* base, const uint32_t* src, uint32_t off,
                                             char* stage, int wave) {
 #pragma unroll
   for (int i = 0; i < N; ++i)
     __builtin_amdgcn_global_load_lds(base + (src[i] + off), stage + (wave + NW * i) * 1024, 16,
-                                     0, 0);
+                                     0, AUX);
 }
 
 // Fragment u of this wave in a stage: A fragments 0..7 (16 rows each) at la + 1024 u, B
@@ -148,6 +149,12 @@ __device__ __forceinline__ void mma_stage(f32x4 (*acc)[8], bf16x8* af, const bf1
 constexpr int kNW = 8;                 // waves: 4 along M x 2 along N
 constexpr int kNT = 64 * kNW;          // threads
 constexpr int kDma = kBM / 8 / kNW;    // 1 KiB DMA instructions per wave per full operand stage
+// Cache policy of the weight DMAs: non-temporal (gfx950 `nt`).  Each expert's weights are
+// read by its M tiles at about the same time and then not again in the launch, so they should
+// not push token rows, H and the expert rows the next kernels read out of L2 and the MALL
+// (measured on MI355X: 35B-A3B decode 289 -> 271 us, prefill 435 -> 418 us, skewed 567 ->
+// 532 us; the sigmoid and 397B-A17B layers' gate_up 1.7% and 2.7% faster).
+constexpr int kWeightAux = 2;
 
 // First row of wave row block wm when blocks 0 and 1 hold mi_hi and blocks 2 and 3 mi_lo
 // 16-row MFMA tiles.
@@ -529,12 +536,12 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int t
     // in flight; a stage of token rows is MI instructions per wave, one of weights kDma.
     lds_barrier();
     dma_operand<kNW, MI>(p.A, srcA, 0, a_at(G0), wave);
-    dma_operand<kNW>(gbase, srcB, 0, b_at(G0), wave);
+    dma_operand<kNW, kDma, kWeightAux>(gbase, srcB, 0, b_at(G0), wave);
     if (ns > 1) {
       dma_operand<kNW, MI>(p.A, srcA, kRow, a_at(G0 + 1), wave);
-      dma_operand<kNW>(gbase, srcB, kRow, b_at(G0 + 1), wave);
+      dma_operand<kNW, kDma, kWeightAux>(gbase, srcB, kRow, b_at(G0 + 1), wave);
     }
-    if (ns > 2) dma_operand<kNW>(gbase, srcB, 2 * kRow, b_at(G0 + 2), wave);
+    if (ns > 2) dma_operand<kNW, kDma, kWeightAux>(gbase, srcB, 2 * kRow, b_at(G0 + 2), wave);
     if (ns > 2)  // A1 B1 B2 were issued after B0 and may still fly
       barrier_after<MI + 2 * kDma, 0>();
     else
@@ -568,7 +575,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int t
                              sB + rb * kBStage + lb_row + cb1, bf1);
     barrier_after<kDma, 0>();  // B(g+2) went out after A(g+1) and may still fly
     dma_operand<kNW, MI>(p.A, srcA, (uint32_t)(g + 2) * kRow, sA + ra * kAS, wave);
-    dma_operand<kNW>(gbase, srcB, (uint32_t)(g + 3) * kRow, sB + rb * kBStage, wave);
+    dma_operand<kNW, kDma, kWeightAux>(gbase, srcB, (uint32_t)(g + 3) * kRow, sB + rb * kBStage, wave);
     if constexpr (MI > 0)
       mma_stage<MI, kSwiglu, PAIR>(acc, af0, bf1, sA + ra1 * kAS + la_row + ch0,
                              sB + rb1 * kBStage + lb_row + cb0, bf0);
@@ -593,7 +600,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int t
     else if (nxt)
       dma_rows_n<kMaxMI>(nx_mi, p.A, nsA, (uint32_t)(g + 2 - ns) * kRow, sA + ra * kAS, wave);
     if (nxt)  // g + 3 >= ns here: the next tile's weights
-      dma_operand<kNW>(p.B + (int64_t)nx.group * p.b_group_bytes, nsB,
+      dma_operand<kNW, kDma, kWeightAux>(p.B + (int64_t)nx.group * p.b_group_bytes, nsB,
                        (uint32_t)(g + 3 - ns) * kRow, sB + rb * kBStage, wave);
     if constexpr (MI > 0) {
       // after the last stage these reads fetch unused leftovers
