@@ -38,6 +38,11 @@ CASES = {
     # (dense tiles; the down GEMM writes fp32 rows, row-scaled by the gate with the atomic combine)
     "shared_wide": ("tiny", {"D": 256, "E": 4, "K": 2, "F": 256, "F_shared": 2048,
                              "shared_gated": True, "dtype": "bf16"}, 2048),
+    # the same with an ungated shared expert and a sigmoid router, a ragged last 256-row tile of
+    # the dense shared GEMMs, and D = 320 (a ragged last column tile and fp16 factor block)
+    "shared_wide_sigmoid": ("tiny", {"D": 320, "E": 6, "K": 3, "F": 192, "F_shared": 2048,
+                                     "shared_gated": False, "scoring": "sigmoid",
+                                     "dtype": "bf16"}, 2000),
     # degenerate routings: every expert selected (dense mixture), a single expert
     "dense_K_eq_E": ("tiny", {"E": 8, "K": 8}, 77),
     "single_expert": ("tiny", {"E": 1, "K": 1, "dtype": "bf16"}, 50),
