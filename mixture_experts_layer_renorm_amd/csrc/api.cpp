@@ -387,9 +387,12 @@ bool compact_rows(const moe_problem* p, moe::TileCfg plan) {
   return p->dtype == MOE_DTYPE_BF16 && plan == moe::TILE_MFMA;
 }
 
-// Shared expert on all T tokens: Hs = SwiGLU gate/up of x; out = row_scale * (Hs Ws_downᵀ).
+// Shared expert on all T tokens: Hs = SwiGLU gate/up of x; out = row_scale * (Hs Ws_downᵀ), as
+// fp32 rows, or (out_scale, matrix-core GEMM only) fp16 rows with one power-of-two factor per
+// row and 128-column block in out_scale [T, ceil(D / 128)].
 hipError_t run_shared(const moe_problem* p, const void* x, const moe_weights* w, void* Hs,
-                      float* out, const float* row_scale, hipStream_t s) {
+                      void* out, const float* row_scale, hipStream_t s,
+                      float* out_scale = nullptr) {
   const size_t es = esize(p->dtype);
   const moe::TileCfg cfg = shared_cfg(p);
   const int bm = moe::tile_bm(cfg);
@@ -417,6 +420,8 @@ hipError_t run_shared(const moe_problem* p, const void* x, const moe_weights* w,
   d.C = out;
   d.ldc = p->D;
   d.row_scale = row_scale;
+  d.c_scale = out_scale;
+  d.ldcs = (p->D + moe::kScaleCols - 1) / moe::kScaleCols;
   return moe::launch_gemm(p->dtype, cfg, moe::EPI_STORE, d, mt, s);
 }
 
@@ -478,7 +483,10 @@ const char* moe_describe_plan(const moe_problem* p) {
   text += (p->flags & MOE_FLAG_ATOMIC_COMBINE)
               ? "; combine: fp32 atomics in the down epilogue"
               : compact_rows(p, grouped_cfg(p))
-                    ? "; combine: gather in slot order over fp16 rows with block factors"
+                    ? (has_shared(p) && shared_cfg(p) == moe::TILE_MFMA
+                           ? "; combine: gather in slot order over fp16 rows with block factors "
+                             "(routed and shared)"
+                           : "; combine: gather in slot order over fp16 rows with block factors")
                     : "; combine: gather in slot order";
   return text.c_str();
 }
@@ -754,12 +762,19 @@ int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_
               "gate_up GEMM launch");
   const float* gate = g ? r.shared_gate : nullptr;
   if (!(p->flags & MOE_FLAG_ATOMIC_COMBINE)) {
-    // 4. shared expert and routed down into fp32 buffers, then the gather combine
+    // 4. shared expert and routed down into row buffers, then the gather combine.  With fp16
+    //    routed rows the shared rows are fp16 with block factors too when the matrix-core GEMM
+    //    runs the shared expert (its epilogue makes them): half the bytes of the shared
+    //    expert's store and of the combine's read of it
     float* y_perm = at<float>(ws, L.y_perm);
-    float* y_shared = has_shared(p) ? at<float>(ws, L.y_shared) : nullptr;
+    void* y_shared = has_shared(p) ? at<void>(ws, L.y_shared) : nullptr;
+    float* ys_scale = nullptr;
+    if (y_shared && compact_rows(p, plan) && shared_cfg(p) == moe::TILE_MFMA)
+      ys_scale = reinterpret_cast<float*>(static_cast<char*>(y_shared) +
+                                          ((p->T * p->D * 2 + 255) / 256) * 256);
     MOE_HIP_TRY(mark(MOE_STAGE_SHARED), "event record");
     if (y_shared)
-      MOE_HIP_TRY(run_shared(p, x, w, at<void>(ws, L.Hs), y_shared, nullptr, s),
+      MOE_HIP_TRY(run_shared(p, x, w, at<void>(ws, L.Hs), y_shared, nullptr, s, ys_scale),
                   "shared expert launch");
     MOE_HIP_TRY(mark(MOE_STAGE_DOWN), "event record");
     if (compact_rows(p, plan)) {
@@ -773,15 +788,16 @@ int forward_impl(const moe_problem* p, const void* x, const moe_weights* w, moe_
                   "down GEMM launch");
       MOE_HIP_TRY(mark(MOE_STAGE_FINAL), "event record");
       MOE_HIP_TRY(moe::launch_combine16(y_perm, y_scale, nblk, r.inv_perm, r.topk_w, y_shared,
-                                        gate, p->T, p->K, p->D, out, p->out_dtype, s),
+                                        ys_scale, gate, p->T, p->K, p->D, out, p->out_dtype, s),
                   "combine launch");
     } else {
       MOE_HIP_TRY(run_down(p, H, w->w_down, tiles, tile_count, L.max_mtiles, plan, y_perm,
                            nullptr, nullptr, nullptr, s),
                   "down GEMM launch");
       MOE_HIP_TRY(mark(MOE_STAGE_FINAL), "event record");
-      MOE_HIP_TRY(moe::launch_combine(y_perm, r.inv_perm, r.topk_w, y_shared, gate, p->T, p->K,
-                                      p->D, out, p->out_dtype, s),
+      MOE_HIP_TRY(moe::launch_combine(y_perm, r.inv_perm, r.topk_w,
+                                      static_cast<const float*>(y_shared), gate, p->T, p->K, p->D,
+                                      out, p->out_dtype, s),
                   "combine launch");
     }
     MOE_HIP_TRY(mark(MOE_STAGE_COUNT), "event record");

@@ -8,6 +8,8 @@
 //           a power-of-two factor per 256-column block.
 // cast    : fp32 accumulator -> output dtype (round to nearest even), for the atomic path.
 // zero    : fill an fp32 accumulator with +0.0 (a kernel, not a memset node).
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace moe {
@@ -70,13 +72,15 @@ __device__ __forceinline__ void store8(__bf16* dst, const float* a) {
 }
 
 // Gather-sum over fp16 expert rows with per-(row, kScaleCols-column block) factors: 8 columns per
-// thread (one 16-byte load per slot), in slot order, then the shared branch, one rounding.
-template <typename OUT>
+// thread (one 16-byte load per slot), in slot order, then the shared branch -- fp32 rows, or
+// (SH16) fp16 rows with the same kind of factors -- each term one fma, one rounding.
+template <typename OUT, bool SH16>
 __global__ void __launch_bounds__(256) combine16_kernel(const _Float16* __restrict__ y16,
                                                         const float* __restrict__ ysc, int nblk,
                                                         const int32_t* __restrict__ inv_perm,
                                                         const float* __restrict__ topk_w,
-                                                        const float* __restrict__ y_shared,
+                                                        const void* __restrict__ y_shared,
+                                                        const float* __restrict__ ys_sc,
                                                         const float* __restrict__ gate, int64_t T,
                                                         int K, int D, OUT* __restrict__ out) {
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -92,19 +96,27 @@ __global__ void __launch_bounds__(256) combine16_kernel(const _Float16* __restri
         const float w = topk_w[t * K + k] * ysc[(int64_t)pos * nblk + d / kScaleCols];
         const f16x8 v = *(const f16x8*)(y16 + (int64_t)pos * D + d);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += w * (float)v[i];
+        for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(w, (float)v[i], acc[i]);
       }
       if (y_shared) {
-        const float4 a = *(const float4*)(y_shared + t * D + d);
-        const float4 b = *(const float4*)(y_shared + t * D + d + 4);
-        acc[0] += g * a.x;
-        acc[1] += g * a.y;
-        acc[2] += g * a.z;
-        acc[3] += g * a.w;
-        acc[4] += g * b.x;
-        acc[5] += g * b.y;
-        acc[6] += g * b.z;
-        acc[7] += g * b.w;
+        if constexpr (SH16) {
+          const float gs = g * ys_sc[t * nblk + d / kScaleCols];
+          const f16x8 v = *(const f16x8*)((const _Float16*)y_shared + t * D + d);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(gs, (float)v[i], acc[i]);
+        } else {
+          const float* ys = (const float*)y_shared;
+          const float4 a = *(const float4*)(ys + t * D + d);
+          const float4 b = *(const float4*)(ys + t * D + d + 4);
+          acc[0] = __builtin_fmaf(g, a.x, acc[0]);
+          acc[1] = __builtin_fmaf(g, a.y, acc[1]);
+          acc[2] = __builtin_fmaf(g, a.z, acc[2]);
+          acc[3] = __builtin_fmaf(g, a.w, acc[3]);
+          acc[4] = __builtin_fmaf(g, b.x, acc[4]);
+          acc[5] = __builtin_fmaf(g, b.y, acc[5]);
+          acc[6] = __builtin_fmaf(g, b.z, acc[6]);
+          acc[7] = __builtin_fmaf(g, b.w, acc[7]);
+        }
       }
       store8(out + t * D + d, acc);
     }
@@ -148,18 +160,24 @@ hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const fl
 }
 
 hipError_t launch_combine16(const void* y16, const float* ysc, int nblk, const int32_t* inv_perm,
-                            const float* topk_w, const float* y_shared, const float* gate,
-                            int64_t T, int K, int D, void* out, int out_dtype,
+                            const float* topk_w, const void* y_shared, const float* ys_sc,
+                            const float* gate, int64_t T, int K, int D, void* out, int out_dtype,
                             hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   const int64_t cap = (int64_t)kCus * 16;
   const dim3 g((unsigned)(T < cap ? T : cap)), b(256);
-  if (out_dtype == 1)
-    hipLaunchKernelGGL(combine16_kernel<__bf16>, g, b, 0, stream, (const _Float16*)y16, ysc, nblk,
-                       inv_perm, topk_w, y_shared, gate, T, K, D, (__bf16*)out);
-  else
-    hipLaunchKernelGGL(combine16_kernel<float>, g, b, 0, stream, (const _Float16*)y16, ysc, nblk,
-                       inv_perm, topk_w, y_shared, gate, T, K, D, (float*)out);
+  const auto go = [&](auto out_t, auto sh16) {
+    using OUT = decltype(out_t);
+    hipLaunchKernelGGL((combine16_kernel<OUT, decltype(sh16)::value>), g, b, 0, stream,
+                       (const _Float16*)y16, ysc, nblk, inv_perm, topk_w, y_shared, ys_sc, gate, T,
+                       K, D, (OUT*)out);
+  };
+  const bool sh16 = y_shared && ys_sc;
+  if (out_dtype == 1) {
+    if (sh16) go(__bf16{}, std::true_type{}); else go(__bf16{}, std::false_type{});
+  } else {
+    if (sh16) go(float{}, std::true_type{}); else go(float{}, std::false_type{});
+  }
   return hipGetLastError();
 }
 

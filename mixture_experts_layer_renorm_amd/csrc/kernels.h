@@ -174,9 +174,11 @@ hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const fl
                           void* out, int out_dtype, hipStream_t stream);
 // The same combine over fp16 expert rows y16 [T*K, D] with block factors ysc [T*K, nblk]
 // (nblk = ceil(D / kScaleCols)); each term is (topk_w * factor) * value, summed in slot order.
+// The shared rows y_shared [T, D] are fp32, or fp16 with block factors ys_sc [T, nblk] when
+// ys_sc is non-null.
 hipError_t launch_combine16(const void* y16, const float* ysc, int nblk, const int32_t* inv_perm,
-                            const float* topk_w, const float* y_shared, const float* gate,
-                            int64_t T, int K, int D, void* out, int out_dtype,
+                            const float* topk_w, const void* y_shared, const float* ys_sc,
+                            const float* gate, int64_t T, int K, int D, void* out, int out_dtype,
                             hipStream_t stream);
 hipError_t launch_cast(const float* src, void* dst, int64_t n, int out_dtype, hipStream_t stream);
 hipError_t launch_zero(float* dst, int64_t n, hipStream_t stream);
