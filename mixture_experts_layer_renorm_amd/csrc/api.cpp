@@ -11,7 +11,7 @@
 #include <mutex>
 #include <string>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "kernels.h"
 
 namespace {
@@ -142,12 +142,17 @@ moe::TileCfg dense_cfg(int64_t M, int64_t N) {
 }
 
 // Router: bf16 batches of up to 1024 tokens use the split-K matrix-core router (partial sums
-// reduced by the top-K kernel), which keeps the latency of a short batch low.  Larger bf16
-// batches use the tile GEMM, whose speed here is set by the bytes its DMA rings keep in flight
-// per CU: 32 x 128 tiles with the reduction split (up to 8 slices of at least 8 K steps, summed
-// in order by the top-K kernel) until two work-groups per CU run; when the 32-row tiles alone
-// exceed that, 256 x 128 tiles (a quarter of the re-reads of the router weights) split until
-// they fill every CU, if they can.  fp32 layers use the tile GEMM unsplit.
+// reduced by the top-K kernel), which keeps the latency of a short batch low.  Longer bf16
+// batches of at least 32 output tiles run on the matrix-core GEMM (dense 256 x 256 tiles;
+// measured on MI355X: 8192 and 16384 tokens 50 us instead of 105 and 75; at 16 tiles, 4096
+// tokens, it was slower than the tile GEMM, 26 vs 20 us) with the reduction split into
+// up to 8 slices of at least 4 stages, until about one work-group per CU runs; the top-K
+// kernel sums the slices in order and computes the shared-gate logit itself (a dot product of
+// the token's row with the gate vector, so no extra output column is needed).  That needs E a
+// multiple of 4 and 32-bit operand offsets; otherwise, and for fp32 layers, the tile GEMM
+// runs: 32 x 128 tiles with the reduction split (up to 8 slices of at least 8 K steps) until
+// two work-groups per CU run; when the 32-row tiles alone exceed that, 256 x 128 tiles split
+// until they fill every CU, if they can (fp32 layers unsplit).
 bool router_split(const moe_problem* p) { return p->dtype == MOE_DTYPE_BF16 && p->T <= 1024; }
 
 struct RouterTiles {
@@ -155,9 +160,25 @@ struct RouterTiles {
   int ks;
 };
 
+bool router_mfma(const moe_problem* p) {
+  const int64_t lim = (int64_t)1 << 32;
+  const int64_t tiles = ((p->T + 255) / 256) * ((p->E + 255) / 256);
+  return p->dtype == MOE_DTYPE_BF16 && p->T > 1024 && tiles >= 32 && p->E % 4 == 0 &&
+         p->T * p->D * 2 < lim && (int64_t)p->E * p->D * 2 < lim &&
+         p->T * p->E < ((int64_t)1 << 31);
+}
+
 RouterTiles router_tiles(const moe_problem* p) {
   const int64_t ncols = p->E + (gated(p) ? 1 : 0);
   if (p->dtype != MOE_DTYPE_BF16) return {dense_cfg(p->T, ncols), 1};
+  if (router_mfma(p)) {
+    const int64_t tiles = ((p->T + 255) / 256) * ((p->E + 255) / 256);
+    const int ns = p->D / 64;  // 64-wide stages of the whole reduction
+    int ks = 1;
+    while (ks * 2 <= 8 && tiles * ks * 2 <= moe::kCus && ns % (ks * 2) == 0 && ns / (ks * 2) >= 4)
+      ks *= 2;
+    return {moe::TILE_MFMA, ks};
+  }
   const int nk = p->D / 64;  // 64-wide K steps of bf16 rows
   const auto split = [&](int64_t tiles, int64_t slots) {
     int ks = 1;
@@ -316,6 +337,15 @@ hipError_t run_router(const moe_problem* p, const void* x, const moe_weights* w,
   ta->gate_src = gate_w ? gate_logit : nullptr;
   ta->gate_ld = 1;
   ta->gate_slice_stride = p->T;
+  if (rt.cfg == moe::TILE_MFMA) {
+    // no extra column: the top-K kernel takes the gate logit from x and the gate vector
+    g.B2 = nullptr;
+    g.C2 = nullptr;
+    ta->gate_src = nullptr;
+    ta->gate_x = gate_w ? (const __bf16*)x : nullptr;
+    ta->gate_w = (const __bf16*)gate_w;
+    ta->D = p->D;
+  }
   const int bm = moe::tile_bm(rt.cfg);
   return moe::launch_gemm(p->dtype, rt.cfg, moe::EPI_STORE, g, (p->T + bm - 1) / bm, s);
 }
@@ -474,7 +504,9 @@ const char* moe_describe_plan(const moe_problem* p) {
   const std::string router =
       router_split(p)
           ? "split-K mfma 16x64, " + std::to_string(router_ks(p)) + " K slice(s)"
-          : name(router_tiles(p).cfg) + ", " + std::to_string(router_tiles(p).ks) + " K slice(s)";
+          : name(router_tiles(p).cfg) + ", " + std::to_string(router_tiles(p).ks) + " K slice(s)" +
+                (router_tiles(p).cfg == moe::TILE_MFMA && gated(p) ? ", gate logit in top-K"
+                                                                   : "");
   text = "router: " + router + "; dispatch: " +
          (moe::dispatch_fused(p->T * p->K, p->E, p->dispatch_kernel) ? "one work-group"
                                                                       : "count, then scan+scatter") +

@@ -73,7 +73,12 @@ __device__ __forceinline__ void store8(__bf16* dst, const float* a) {
 
 // Gather-sum over fp16 expert rows with per-(row, kScaleCols-column block) factors: 8 columns per
 // thread (one 16-byte load per slot), in slot order, then the shared branch -- fp32 rows, or
-// (SH16) fp16 rows with the same kind of factors -- each term one fma, one rounding.
+// (SH16) fp16 rows with the same kind of factors -- each term one fma, one rounding.  The slots
+// are taken 8 at a time: their positions and weights are uniform loads, and the 8 row chunks
+// and factors are all requested before the first is added, so each wave keeps 8 row loads in
+// flight instead of one (the sum is still formed in slot order).
+constexpr int kSlotBatch = 8;
+
 template <typename OUT, bool SH16>
 __global__ void __launch_bounds__(256) combine16_kernel(const _Float16* __restrict__ y16,
                                                         const float* __restrict__ ysc, int nblk,
@@ -90,33 +95,55 @@ __global__ void __launch_bounds__(256) combine16_kernel(const _Float16* __restri
       float acc[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-      for (int k = 0; k < K; ++k) {
-        const int pos = inv_perm[t * K + k];
-        if (pos < 0) continue;  // sentinel or dropped assignment
-        const float w = topk_w[t * K + k] * ysc[(int64_t)pos * nblk + d / kScaleCols];
-        const f16x8 v = *(const f16x8*)(y16 + (int64_t)pos * D + d);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(w, (float)v[i], acc[i]);
-      }
+      const int blk = d / kScaleCols;
+      // the shared branch's row goes out with the first batch of slot loads
+      float sh[8], gs = g;
       if (y_shared) {
         if constexpr (SH16) {
-          const float gs = g * ys_sc[t * nblk + d / kScaleCols];
+          gs = g * ys_sc[t * nblk + blk];
           const f16x8 v = *(const f16x8*)((const _Float16*)y_shared + t * D + d);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(gs, (float)v[i], acc[i]);
+          for (int i = 0; i < 8; ++i) sh[i] = (float)v[i];
         } else {
           const float* ys = (const float*)y_shared;
           const float4 a = *(const float4*)(ys + t * D + d);
           const float4 b = *(const float4*)(ys + t * D + d + 4);
-          acc[0] = __builtin_fmaf(g, a.x, acc[0]);
-          acc[1] = __builtin_fmaf(g, a.y, acc[1]);
-          acc[2] = __builtin_fmaf(g, a.z, acc[2]);
-          acc[3] = __builtin_fmaf(g, a.w, acc[3]);
-          acc[4] = __builtin_fmaf(g, b.x, acc[4]);
-          acc[5] = __builtin_fmaf(g, b.y, acc[5]);
-          acc[6] = __builtin_fmaf(g, b.z, acc[6]);
-          acc[7] = __builtin_fmaf(g, b.w, acc[7]);
+          sh[0] = a.x; sh[1] = a.y; sh[2] = a.z; sh[3] = a.w;
+          sh[4] = b.x; sh[5] = b.y; sh[6] = b.z; sh[7] = b.w;
         }
+      }
+      for (int k0 = 0; k0 < K; k0 += kSlotBatch) {
+        int pos[kSlotBatch];
+        float w[kSlotBatch];
+#pragma unroll
+        for (int u = 0; u < kSlotBatch; ++u) {
+          const int k = k0 + u;
+          pos[u] = k < K ? inv_perm[t * K + k] : -1;
+          w[u] = k < K ? topk_w[t * K + k] : 0.0f;
+        }
+        f16x8 v[kSlotBatch];
+        float sc[kSlotBatch];
+#pragma unroll
+        for (int u = 0; u < kSlotBatch; ++u) {
+          // a sentinel, dropped or past-K slot (pos < 0) reads row 0 and is not added: loads
+          // without branches between them go out back to back
+          const int64_t row = pos[u] < 0 ? 0 : pos[u];
+          sc[u] = ysc[row * nblk + blk];
+          v[u] = *(const f16x8*)(y16 + row * D + d);
+        }
+#pragma unroll
+        for (int u = 0; u < kSlotBatch; ++u) {
+          const float wu = w[u] * sc[u];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float a = __builtin_fmaf(wu, (float)v[u][i], acc[i]);
+            acc[i] = pos[u] < 0 ? acc[i] : a;
+          }
+        }
+      }
+      if (y_shared) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(gs, sh[i], acc[i]);
       }
       store8(out + t * D + d, acc);
     }

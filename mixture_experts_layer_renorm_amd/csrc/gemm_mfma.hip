@@ -173,12 +173,17 @@ __device__ __forceinline__ void tile_mi(int rows, int* mi_hi, int* mi_lo) {
 // A tile of a work-group's schedule: its group (expert), rows [row_start, + rows) and N tile.
 struct TileMap {
   int group, row_start, rows, n_tile;
+  uint32_t k0;  // first byte of each row this tile reduces over (split-K slice * slice bytes)
+  int slice;
 };
 
 // Logical tile t: expert-major, then N tile, then M tile (the M tiles of one expert are
 // entries [first, first + cnt) of the tile map and own logical tiles [first·ntN, (first+cnt)·ntN));
 // dense mode (no tile map) has one group of mt_total M tiles.  Decoding takes two dependent
 // rounds of scalar loads: the expert's entry (map_expert), then the M tile's (map_mtile).
+// (Cutting dense mode into groups of a few M tiles, so that an XCD streams only its own token
+// rows, made the dense shared expert about 1% faster but cost the grouped kernels scalar
+// registers, and the sigmoid layer's routed gate_up 2.8%.)
 __device__ __forceinline__ void map_expert(const GemmParams& p, int t, int ntN, int mt_total,
                                            int* first, int* cnt) {
   if (p.tiles) {
@@ -280,11 +285,29 @@ __device__ __forceinline__ uint32_t gather_source(const GemmParams& p, int lane,
   return (uint32_t)(a / p.a_div) * (uint32_t)p.lda_bytes + lane_chunk(lane, wave) * 16;
 }
 
+// Split-K (KS variant: dense fp32 rows, the router): the reduction is cut into p.k_slices
+// equal slices and logical tile t covers slice t / (mt_total ntN) of output tile
+// t % (mt_total ntN), so an XCD's share of the sequence mostly stays within one slice and its
+// tiles share that slice of the weights.  Other variants have one slice at compile time.
+template <bool KS>
+__device__ __forceinline__ int k_slices(const GemmParams& p) {
+  if constexpr (KS) return p.k_slices > 1 ? p.k_slices : 1;
+  return 1;
+}
+
+template <bool KS>
 __device__ __forceinline__ void load_map(const GemmParams& p, int t, int ntN, int mt_total,
                                          TileMap& tile) {
+  int slice = 0;
+  if constexpr (KS) {
+    slice = t / (mt_total * ntN);
+    t -= slice * mt_total * ntN;
+  }
   int first, cnt;
   map_expert(p, t, ntN, mt_total, &first, &cnt);
   map_mtile(p, t, ntN, first, cnt, tile);
+  tile.slice = slice;
+  tile.k0 = KS ? (uint32_t)slice * (uint32_t)(p.Kdim / k_slices<KS>(p)) * 2u : 0u;  // bf16 bytes
 }
 
 // Every DMA source of a tile: weight rows, and token rows of the first NA instructions (the
@@ -300,8 +323,12 @@ __device__ __forceinline__ void tile_sources(const GemmParams& p, int lane, int 
 #pragma unroll
     for (int i = 0; i < NA; ++i) sa[i] = gather_source(p, lane, wave, v[i]);
   } else {
+    // dense rows; a split-K tile starts its rows at byte k0 (0 without a split)
 #pragma unroll
-    for (int i = 0; i < NA; ++i) sa[i] = row_source(p, lane, wave, tile.row_start, tile.rows, i);
+    for (int i = 0; i < NA; ++i)
+      sa[i] = row_source(p, lane, wave, tile.row_start, tile.rows, i) + tile.k0;
+#pragma unroll
+    for (int i = 0; i < kDma; ++i) sb[i] += tile.k0;
   }
 }
 
@@ -323,10 +350,10 @@ __device__ __forceinline__ void dma_rows_n(int n, const char* base, const uint32
 // in the paired layout columns 32 m + 8 lk + [0, 8) over tiles j = 2m, 2m + 1 (bf16 H and
 // fp16 rows: 16-byte stores, 64-byte row runs, half the store instructions).  L2 merges the
 // runs into whole lines.  No LDS, no barrier.
-template <int MI, int EPI, bool RS, bool PAIR>
+template <int MI, int EPI, bool RS, bool PAIR, bool KS>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x4 (*acc)[8], int lane,
                                            int wn, int wrow0, int row_start, int rows,
-                                           int n_tile) {
+                                           int n_tile, int slice) {
   typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   const int lr = lane & 15, lk = lane >> 4;
@@ -414,12 +441,15 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x4 (*ac
   } else if constexpr (EPI == EPI_STORE) {
     // fp32, times row_scale[row] in the RS variant (its vector load is waited for at once,
     // which also waits for the next tile's first stages; the variant serves only the
-    // row-scaled shared expert)
+    // row-scaled shared expert).  A split-K tile writes its partial sums to its slice's plane,
+    // and slice 0 adds col_bias.
     static_assert(!PAIR, "fp32 rows use the plain layout");
     const int c4 = 4 * lk;
     const int ncols = min(kBN, p.N - n_tile * kBN);
     const int c0 = wn * 128;
-    float* Ct = (float*)p.C + (int64_t)row_start * p.ldc + n_tile * kBN;
+    float* Ct = (float*)p.C + slice * p.c_slice_stride + (int64_t)row_start * p.ldc +
+                n_tile * kBN;
+    const float* bias = KS && slice == 0 && p.col_bias ? p.col_bias + n_tile * kBN : nullptr;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int row = wrow0 + 16 * i + lr;
@@ -431,6 +461,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x4 (*ac
           const int col = c0 + 16 * j + c4;
           if (col < ncols) {
             f32x4 v = acc[i][j];
+            if (bias) v += *(const f32x4*)(bias + col);
             if constexpr (RS) v *= s;
             *(f32x4*)(Ct + (int64_t)row * p.ldc + col) = v;
           }
@@ -476,7 +507,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x4 (*ac
 // describe it, nx_group < 0 if there is none, and nx_mi is this wave's MI there), and that
 // tile then starts with them in flight or landed (`pre`), so the weight stream does not stop
 // for an epilogue or a prologue.
-template <int MI, int EPI, int AROWS, bool RS, bool PAIR>
+template <int MI, int EPI, int AROWS, bool RS, bool PAIR, bool KS>
 __device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int tid, int wave,
                                           const TileMap& cur, int ns, int mi_hi, int mi_lo,
                                           int G0, bool pre, int tn, int ntN, int mt_total,
@@ -517,7 +548,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int t
   const bool nxt = tn >= 0;
   int nx_mi = 0;  // this wave's token-row DMA instructions per stage of the next tile
   if (nxt) {
-    load_map(p, tn, ntN, mt_total, nx);
+    load_map<KS>(p, tn, ntN, mt_total, nx);
     tile_sources<kSwiglu, PAIR, kMaxMI>(p, lane, wave, nx, nsA, nsB);
     int nh, nl;
     tile_mi(nx.rows, &nh, &nl);
@@ -618,7 +649,8 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int t
   int elane = lane;
   asm volatile("" : "+v"(elane));
   if constexpr (MI > 0)
-    store_tile<MI, EPI, RS, PAIR>(p, acc, elane, wn, wrow0, cur.row_start, rows, cur.n_tile);
+    store_tile<MI, EPI, RS, PAIR, KS>(p, acc, elane, wn, wrow0, cur.row_start, rows, cur.n_tile,
+                                  cur.slice);
 }
 
 // Persistent, XCD-aware work-groups over the logical tiles: XCD x (work-groups b with
@@ -626,7 +658,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams& p, char* smem, int t
 // AROWS = 256 rows per token-row stage (any tile), or 64 when no tile has more than 64 rows
 // (decode batches: 8 KiB stages); RS: the STORE epilogue multiplies by row_scale; PAIR: the
 // paired column layout (SwiGLU and fp16 rows, see boff).
-template <int EPI, int AROWS, bool RS, bool PAIR>
+template <int EPI, int AROWS, bool RS, bool PAIR, bool KS>
 __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mfma_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[kSA * AROWS * kRow + kSB * kBStage];
@@ -635,10 +667,10 @@ mfma_kernel(const GemmParams p) {
   constexpr int BNE = EPI == EPI_SWIGLU ? kBN / 2 : kBN;  // output columns per tile
   const int ntN = (p.N + BNE - 1) / BNE;
   const int mt_total = p.tiles ? load_uniform(p.tile_count, 0) : (p.M + kBM - 1) / kBM;
-  const int nt = mt_total * ntN;
+  const int nt = mt_total * ntN * k_slices<KS>(p);
   const int xcd = blockIdx.x % kXcds, per = gridDim.x / kXcds, jb = blockIdx.x / kXcds;
   const int lo = (int)((int64_t)nt * xcd / kXcds), hi = (int)((int64_t)nt * (xcd + 1) / kXcds);
-  const int ns = p.Kdim / 64;  // DMA stages (Kdim is a multiple of 64)
+  const int ns = p.Kdim / 64 / k_slices<KS>(p);  // DMA stages per tile (host-checked divisor)
 
   // The next tile's stages 0-2 come with this tile's last three refills, which needs three
   // stages per tile; shorter reductions run each tile with its own prologue.  A tile's map
@@ -646,7 +678,7 @@ mfma_kernel(const GemmParams p) {
   const bool cross = ns >= 3;
   int t = lo + jb;
   TileMap cur, nx;
-  if (t < hi) load_map(p, t, ntN, mt_total, cur);
+  if (t < hi) load_map<KS>(p, t, ntN, mt_total, cur);
   int G0 = 0;
   for (; t < hi; t += per) {
     const int tn = cross && t + per < hi ? t + per : -1;
@@ -654,7 +686,7 @@ mfma_kernel(const GemmParams p) {
     tile_mi(cur.rows, &mi_hi, &mi_lo);
     const bool pre = cross && G0 > 0;
     const auto run = [&](auto mi) {
-      ring_tile<decltype(mi)::value, EPI, AROWS, RS, PAIR>(p, smem, tid, wave, cur, ns, mi_hi, mi_lo,
+      ring_tile<decltype(mi)::value, EPI, AROWS, RS, PAIR, KS>(p, smem, tid, wave, cur, ns, mi_hi, mi_lo,
                                                      G0, pre, tn, ntN, mt_total, nx);
     };
     using I0 = std::integral_constant<int, 0>;
@@ -675,7 +707,7 @@ mfma_kernel(const GemmParams p) {
     if (tn >= 0)
       cur = nx;
     else if (t + per < hi)
-      load_map(p, t + per, ntN, mt_total, cur);
+      load_map<KS>(p, t + per, ntN, mt_total, cur);
   }
 }
 
@@ -685,7 +717,8 @@ template <int EPI>
 hipError_t launch_epi(const GemmParams& p, int64_t max_mtiles, hipStream_t stream) {
   constexpr int BNE = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
   const int64_t ntN = (p.N + BNE - 1) / BNE;
-  const int64_t want = max_mtiles * ntN;
+  const int64_t ks = (!p.tiles && p.k_slices > 1) ? p.k_slices : 1;
+  const int64_t want = max_mtiles * ntN * ks;
   int64_t grid = want < kCus ? want : kCus;
   grid = ((grid + kXcds - 1) / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
@@ -693,28 +726,31 @@ hipError_t launch_epi(const GemmParams& p, int64_t max_mtiles, hipStream_t strea
                              : p.M <= kSmallRows;
   const dim3 g((unsigned)grid), b(kNT);
   // layout and epilogue variants: SwiGLU and fp16 rows paired, fp32 rows (optionally
-  // row-scaled) and the atomic combine plain
-  const auto go = [&](auto rs, auto pair) {
+  // row-scaled, or split-K with a column bias) and the atomic combine plain
+  const auto go = [&](auto rs, auto pair, auto ksplit) {
     constexpr bool RS = decltype(rs)::value, PAIR = decltype(pair)::value;
+    constexpr bool KS = decltype(ksplit)::value;
     if (small)
-      hipLaunchKernelGGL((mfma_kernel<EPI, kSmallRows, RS, PAIR>), g, b, 0, stream, p);
+      hipLaunchKernelGGL((mfma_kernel<EPI, kSmallRows, RS, PAIR, KS>), g, b, 0, stream, p);
     else
-      hipLaunchKernelGGL((mfma_kernel<EPI, kBM, RS, PAIR>), g, b, 0, stream, p);
+      hipLaunchKernelGGL((mfma_kernel<EPI, kBM, RS, PAIR, KS>), g, b, 0, stream, p);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
   if constexpr (EPI == EPI_SWIGLU) {
-    go(F_{}, T_{});
+    go(F_{}, T_{}, F_{});
   } else if constexpr (EPI == EPI_STORE) {
     if (p.c_scale && p.row_scale) return hipErrorInvalidValue;  // no row-scaled fp16 rows
     if (p.c_scale)
-      go(F_{}, T_{});
+      go(F_{}, T_{}, F_{});
     else if (p.row_scale)
-      go(T_{}, F_{});
+      go(T_{}, F_{}, F_{});
+    else if (p.k_slices > 1 || p.col_bias)
+      go(F_{}, F_{}, T_{});
     else
-      go(F_{}, F_{});
+      go(F_{}, F_{}, F_{});
   } else {
-    go(F_{}, F_{});
+    go(F_{}, F_{}, F_{});
   }
   return hipGetLastError();
 }
@@ -724,7 +760,14 @@ hipError_t launch_epi(const GemmParams& p, int64_t max_mtiles, hipStream_t strea
 hipError_t launch_mfma_gemm(Epilogue epi, const GemmParams& p, int64_t max_mtiles,
                             hipStream_t stream) {
   if (max_mtiles <= 0) return hipSuccess;
-  if (p.B2 || p.col_bias) return hipErrorInvalidValue;  // router-only features
+  if (p.B2) return hipErrorInvalidValue;  // the extra weight row is the tile GEMM's
+  // split-K and the column bias: dense fp32 rows only, whole 64-wide stages per slice, and
+  // 4-column groups that stay inside a row (f32x4 stores and bias loads)
+  const bool plain_f32 = epi == EPI_STORE && !p.c_scale && !p.row_scale && !p.tiles;
+  if ((p.col_bias || p.k_slices > 1) && !(plain_f32 && p.N % 4 == 0 && p.ldc % 4 == 0))
+    return hipErrorInvalidValue;
+  if (p.k_slices > 1 && (p.Kdim % (64 * p.k_slices) != 0 || p.c_slice_stride % 4 != 0))
+    return hipErrorInvalidValue;
   switch (epi) {
     case EPI_SWIGLU:
       return launch_epi<EPI_SWIGLU>(p, max_mtiles, stream);

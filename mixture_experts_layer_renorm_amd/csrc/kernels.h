@@ -75,7 +75,8 @@ struct GemmParams {
 enum TileCfg : int {
   TILE_SMALL = 0,       // tile GEMM, BM=32,  BN=128
   TILE_LARGE = 1,       // tile GEMM, BM=256, BN=128
-  TILE_MFMA = 2,        // matrix-core GEMM, 256 x 256 tiles, bf16 only, no B2 / col_bias
+  TILE_MFMA = 2,        // matrix-core GEMM, 256 x 256 tiles, bf16 only, no B2; col_bias and
+                        // k_slices for dense fp32 rows only
 };
 int tile_bm(TileCfg cfg);
 int tile_bn(TileCfg cfg);
@@ -92,7 +93,8 @@ hipError_t launch_gemm(int dtype, TileCfg cfg, Epilogue epi, const GemmParams& p
 // t * ld + e] over q < ks (ks = 1: src is the logits matrix).  Writes idx/w [T, K]; optionally
 // the summed logits [T, E] to logits_out, the selection keys [T, E] (the logit, or with
 // sel_bias the fp32 score + bias) to keys_out, and sigmoid of the gate logit (same summation
-// over gate_src[q * gate_slice_stride + t * gate_ld]) to gate_out [T].
+// over gate_src[q * gate_slice_stride + t * gate_ld], or the dot product of gate_x[t] and
+// gate_w when gate_x is set) to gate_out [T].
 struct TopkArgs {
   const float* src;
   int ks;
@@ -108,6 +110,9 @@ struct TopkArgs {
   int64_t gate_ld;
   int64_t gate_slice_stride;
   float* gate_out;
+  const __bf16* gate_x;   // if set (bf16 layers): the gate logit is x[t] . gate_w over D,
+  const __bf16* gate_w;   // computed here instead of read from gate_src
+  int D;
   const float* sel_bias;  // [E] or null: choose on score + bias, weight with the score
 };
 hipError_t launch_update_select_bias(const int32_t* counts, int E, float* bias, float gamma,

@@ -2,7 +2,7 @@
 // loop.  They measure the two roofline ceilings of the layer's kernels on the running GPU, at
 // the clock it holds under that load ("S23-J10" §3: a grouped GEMM over expert weights is bound
 // by reading them when each expert sees few rows, by the matrix cores when it sees hundreds).
-#include "../../include/moe_peaks.h"
+#include "moe_peaks.h"
 #include "kernels.h"
 
 namespace moe {

@@ -1,11 +1,12 @@
 // Router scoring, top-K selection and renormalisation ("MoE" §2 Router; "1.6 混合专家（MoE）"
 // §二 Top-k 门控公式 steps 2-3).
 //
-// One wave64 per token.  Lane l holds logits l, l+64, ... as 64-bit keys
-//   (order-preserving image of the fp32 logit) << 32 | (0xFFFFFFFF - expert id)
-// so one unsigned max picks the largest logit and, among equal logits, the lowest id.  NaN is
-// mapped to -inf's key and -0.0 to +0.0's key before packing.  K rounds of a butterfly max
-// over the wave select the experts in descending order; the winner's key is cleared.
+// One wave64 per token.  Lane l holds logits l, l+64, ... as 32-bit keys, the
+// order-preserving image of the fp32 logit (NaN mapped to -inf's key, -0.0 to +0.0's).  Each
+// of K rounds takes the wave's largest key with a DPP max and then, with one ballot per held
+// slot, the lowest expert id among the lanes holding it, so experts are selected in descending
+// order with ties going to the lower id; the winner's key is cleared to 0, below every real
+// key (padding slots past E hold 0 from the start).
 //
 // Selection compares logits, not probabilities: softmax and sigmoid are strictly increasing,
 // so the top-K set is the same, and the choice does not depend on exp/sigmoid rounding.
@@ -28,14 +29,12 @@ __device__ __forceinline__ float key_value(uint32_t o) {
   return __uint_as_float(u);
 }
 
-// One DPP step of a 64-bit wave max: v and the lane's DPP partner's value (rows outside
-// ROW_MASK keep their own).
+// One DPP step of a 32-bit wave max: v and the lane's DPP partner's value.  Lanes in rows
+// outside ROW_MASK read 0, the identity of an unsigned max, so they keep their own value (and
+// the move folds into a v_max_u32 with a DPP operand).
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ unsigned long long max_dpp_u64(unsigned long long v) {
-  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false);
-  const unsigned long long o = ((unsigned long long)ohi << 32) | olo;
+__device__ __forceinline__ uint32_t max_dpp_u32(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
   return o > v ? o : v;
 }
 
@@ -43,16 +42,14 @@ __device__ __forceinline__ unsigned long long max_dpp_u64(unsigned long long v) 
 // rows of 16 (half-mirror, mirror), then row 0's and 1's maxima carried into rows 1 and 3 and
 // row 1's into rows 2 and 3 (row broadcasts), leaving the wave's maximum in lane 63.  A max
 // does not depend on the order of its operands, so this is exact.
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-  v = max_dpp_u64<0xB1, 0xf>(v);   // quad_perm [1, 0, 3, 2]
-  v = max_dpp_u64<0x4E, 0xf>(v);   // quad_perm [2, 3, 0, 1]
-  v = max_dpp_u64<0x141, 0xf>(v);  // row_half_mirror
-  v = max_dpp_u64<0x140, 0xf>(v);  // row_mirror
-  v = max_dpp_u64<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
-  v = max_dpp_u64<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-  return ((unsigned long long)hi << 32) | lo;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max_dpp_u32<0xB1, 0xf>(v);   // quad_perm [1, 0, 3, 2]
+  v = max_dpp_u32<0x4E, 0xf>(v);   // quad_perm [2, 3, 0, 1]
+  v = max_dpp_u32<0x141, 0xf>(v);  // row_half_mirror
+  v = max_dpp_u32<0x140, 0xf>(v);  // row_mirror
+  v = max_dpp_u32<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = max_dpp_u32<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ float wave_max_f(float v) {
@@ -77,7 +74,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const TopkArgs a) {
   const int E = a.E, K = a.K;
 
   // logit e = the router's partial sums over K slices, added in slice order
-  unsigned long long key[NPL];
+  uint32_t key[NPL];
   float val[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
@@ -101,8 +98,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const TopkArgs a) {
       if (a.logits_out) a.logits_out[t * E + e] = v;
     }
     val[j] = v;
-    key[j] = e < E ? ((unsigned long long)order_key(v) << 32) | (0xFFFFFFFFu - (uint32_t)e)
-                   : 0ull;  // below every real key
+    key[j] = e < E ? order_key(v) : 0u;  // 0: below every real key (-inf's is 0x007FFFFF)
     if (a.keys_out && !a.sel_bias && e < E) a.keys_out[t * E + e] = v;
   }
 
@@ -134,7 +130,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const TopkArgs a) {
       const int e = lane + 64 * j;
       if (e < E) {
         const float kv = sc[j] + a.sel_bias[e];
-        key[j] = ((unsigned long long)order_key(kv) << 32) | (0xFFFFFFFFu - (uint32_t)e);
+        key[j] = order_key(kv);
         if (a.keys_out) a.keys_out[t * E + e] = kv;
       }
     }
@@ -144,25 +140,36 @@ __global__ void __launch_bounds__(256) topk_kernel(const TopkArgs a) {
   float top = 0.0f, my_val = 0.0f;
   int my_id = 0;
   for (int k = 0; k < K; ++k) {
-    unsigned long long best = key[0];
+    uint32_t best = key[0];
 #pragma unroll
     for (int j = 1; j < NPL; ++j) best = key[j] > best ? key[j] : best;
-    best = wave_max_u64(best);
-    const uint32_t e = 0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull);
-    const float v = key_value((uint32_t)(best >> 32));
+    best = wave_max_u32(best);
+    // the lowest id holding the best key: the first slot with a hit, its lowest lane
+    int slot = 0;
+    unsigned long long hit = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      if (hit == 0) {
+        hit = __ballot(key[j] == best);
+        slot = j;
+      }
+    }
+    const int owner = __builtin_ctzll(hit);
+    const uint32_t e = (uint32_t)(64 * slot + owner);
+    const float v = key_value(best);
     if (k == 0) top = v;
-    if ((int)(e & 63u) == lane) {
+    if (lane == owner) {
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
-        if (j == (int)(e >> 6)) key[j] = 0ull;
+        if (j == slot) key[j] = 0u;
     }
     float mv = v;
     if (a.sel_bias) {  // the selected expert's unbiased score, from the lane that holds it
       float own = 0.0f;
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
-        if (j == (int)(e >> 6)) own = sc[j];
-      mv = __shfl(own, (int)(e & 63u), 64);
+        if (j == slot) own = sc[j];
+      mv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, own), owner));
     }
     if (lane == k) {
       my_val = mv;
@@ -190,10 +197,26 @@ __global__ void __launch_bounds__(256) topk_kernel(const TopkArgs a) {
     a.idx[t * K + lane] = my_id;
     a.w[t * K + lane] = s / denom;
   }
-  if (a.gate_out && lane == 0) {
-    float g = a.gate_src[t * a.gate_ld];
-    for (int q = 1; q < a.ks; ++q) g += a.gate_src[q * a.gate_slice_stride + t * a.gate_ld];
-    a.gate_out[t] = 1.0f / (1.0f + expf(-g));
+  if (a.gate_out) {
+    float g;
+    if (a.gate_x) {
+      // gate logit x[t] . w_s: lane l takes elements 8 l + 512 c, c = 0, 1, ...; each lane's
+      // products in order, then a butterfly over the wave (a fixed order, so deterministic)
+      typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+      const __bf16* xr = a.gate_x + t * a.D;
+      float part = 0.0f;
+      for (int d = 8 * lane; d < a.D; d += 512) {
+        const bf16x8 xv = *(const bf16x8*)(xr + d);
+        const bf16x8 wv = *(const bf16x8*)(a.gate_w + d);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part = __builtin_fmaf((float)xv[i], (float)wv[i], part);
+      }
+      g = wave_sum(part);
+    } else {
+      g = a.gate_src[t * a.gate_ld];
+      for (int q = 1; q < a.ks; ++q) g += a.gate_src[q * a.gate_slice_stride + t * a.gate_ld];
+    }
+    if (lane == 0) a.gate_out[t] = 1.0f / (1.0f + expf(-g));
   }
 }
 

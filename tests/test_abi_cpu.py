@@ -112,6 +112,32 @@ def test_plan_choices_and_32bit_offset_limits():
     assert "one work-group" in _plan(T=100000, dispatch_kernel="one_workgroup")
 
 
+def test_router_plan():
+    """Router choice (moe_describe_plan, no GPU): the split-K router for bf16 batches of up to
+    1024 tokens; the matrix-core GEMM with the reduction split until about one work-group per
+    CU (at most 8 slices of at least 4 stages) for longer bf16 batches of at least 32 output
+    tiles, the shared-gate logit
+    then computed in the top-K kernel; the tile GEMM when E is not a multiple of 4, when x
+    reaches 4 GiB, and for fp32 layers."""
+    sig = dict(dtype="bf16", T=16384, D=4096, E=256, K=6, F=2048, F_shared=2048)
+    assert "router: mfma 256x256, 4 K slice(s);" in _plan(**sig)      # 64 tiles x 4
+    gated = dict(dtype="bf16", T=8192, D=4096, E=512, K=10, F=1024, F_shared=1024,
+                 shared_gated=1)
+    assert "router: mfma 256x256, 4 K slice(s), gate logit in top-K;" in _plan(**gated)
+    # 32 tiles: 8 slices of 4 stages (D = 2048)
+    assert "router: mfma 256x256, 8 K slice(s);" in _plan(dtype="bf16", T=8192, D=2048, E=256,
+                                                           K=8, F=512)
+    # D = 256 has 4 stages: no split
+    assert "router: mfma 256x256, 1 K slice(s);" in _plan(dtype="bf16", T=8192, D=256, E=8, K=2,
+                                                           F=64)
+    # fewer than 32 output tiles (4096 tokens, 256 experts: 16) stay on the tile GEMM
+    assert "router: tile 32x128" in _plan(dtype="bf16", T=4096, D=2048, E=256, K=8, F=512)
+    assert "router: split-K mfma 16x64" in _plan(dtype="bf16", T=1024, D=4096, E=256, K=6, F=256)
+    assert "router: tile" in _plan(dtype="bf16", T=8192, D=256, E=6, K=2, F=64)   # E % 4
+    assert "router: tile" in _plan(dtype="bf16", T=1 << 19, D=4096, E=8, K=1, F=256)  # 4 GiB x
+    assert "router: tile" in _plan(T=4096)                                          # fp32
+
+
 def _ws_size(lib, p):
     n = ctypes.c_size_t(0)
     st = lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n))

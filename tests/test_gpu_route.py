@@ -97,14 +97,18 @@ def _fp32_logit_bound(X, W, logits64):
 
 # bf16 batches of up to 1024 tokens take the split-K router (K slices summed by the top-K
 # kernel: 8 slices at T=64, 4 for the gated 513-column a17b router at T=70, 1 past 256 blocks);
-# larger bf16 batches take the tile GEMM with its reduction split into up to 8 slices (4 at
-# T=1025 with a ragged last M tile, 2 for the gated 513-column a17b router at T=1100 and at
-# T=3000 of the sigmoid layer, 1 at T=2000 of a17b), fp32 the unsplit tile GEMM.
+# larger bf16 batches with fewer than 32 output tiles take the tile GEMM with its reduction
+# split into up to 8 slices (4 at T=1025 with a ragged last M tile, 2 for the gated
+# 513-column a17b router at T=1100 and at T=3000 of the sigmoid layer, 1 at T=2000 of a17b),
+# and from 32 tiles the matrix-core GEMM split into 8 slices (ragged last M tiles at T=8000 of
+# the sigmoid layer and T=4000 of the gated a17b layer, whose gate logit the top-K kernel
+# computes; the skewed layer's logit bias at T=8192); fp32 takes the unsplit tile GEMM.
 @pytest.mark.parametrize("name,T", [("tiny", 64), ("a3b_prefill", 333), ("a17b", 70),
                                     ("skew", 200), ("ds_sigmoid", 90), ("a3b_decode", 64),
                                     ("a3b_prefill", 1), ("a17b", 1), ("a3b_prefill", 1024),
                                     ("a3b_prefill", 1025), ("a17b", 1100), ("a17b", 2000),
-                                    ("skew", 4096), ("ds_sigmoid", 3000)])
+                                    ("skew", 4096), ("ds_sigmoid", 3000), ("ds_sigmoid", 8000),
+                                    ("a17b", 4000), ("skew", 8192)])
 def test_router_gemm_and_topk(name, T):
     cfg = CONFIGS[name]
     # only the router's tensors, drawn on the CPU at the workload's real widths
@@ -118,6 +122,10 @@ def test_router_gemm_and_topk(name, T):
         bias = torch.zeros(cfg.E)
         bias[[i * cfg.hot_stride for i in range(cfg.n_hot)]] = cfg.hot_bias
     p = problem_for(cfg, T=T)
+    plan = abi.describe_plan(p)
+    tiles = -(-T // 256) * -(-cfg.E // 256)
+    if cfg.dtype == "bf16" and T > 1024 and tiles >= 32:
+        assert plan.startswith("router: mfma 256x256, 8 K slice(s)"), plan
     r = abi.alloc_routing(p, DEV)
     weights = {"w_router": wr.to(DEV), "logit_bias": None if bias is None else bias.to(DEV),
                "ws_gate": None if ws is None else ws.to(DEV)}
