@@ -95,7 +95,10 @@ __global__ void __launch_bounds__(256) count_kernel(const int32_t* __restrict__ 
 // 0}.  An expert's rows are split evenly over its ceil(c / bm) M tiles (the first c % mt tiles
 // one row more): its tiles then cost the same, run in step on one XCD and fetch each weight
 // tile once into its L2 for all of them (a full tile and a short last one drift apart, and
-// each streams the weights from memory by itself).
+// each streams the weights from memory by itself).  Splitting in whole 32-row pairs instead
+// (390 rows as 224 + 166, 13 pairs, not 195 + 195, 14 pairs) saves MFMAs but lets the tiles
+// drift by a pair in seven: measured on MI355X it made the sigmoid layer's grouped GEMMs 24%
+// slower.
 template <int NT>
 __device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, int bm, int* scratch,
                             int32_t* tiles, int32_t* tile_count) {
