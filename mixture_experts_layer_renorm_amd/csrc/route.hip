@@ -12,6 +12,8 @@
 // so the top-K set is the same, and the choice does not depend on exp/sigmoid rounding.
 // Softmax weights use only the K selected logits: the full-E denominator cancels in
 // p_e / sum_{j in I} p_j, leaving exp(r_e - r_max) / sum_{j in I} exp(r_j - r_max).
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace moe {
@@ -66,7 +68,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 constexpr int kMaxSlices = 8;  // router K slices summed by the top-K kernel
 
-template <int NPL>  // logits held per lane: ceil(E / 64)
+// NPL: logits held per lane, ceil(E / 64); KSM: slices loaded per logit, a.ks rounded up to a
+// power of two (the routers' slice counts are powers of two, so no slice is loaded twice)
+template <int NPL, int KSM>
 __global__ void __launch_bounds__(256) topk_kernel(const TopkArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -83,18 +87,13 @@ __global__ void __launch_bounds__(256) topk_kernel(const TopkArgs a) {
     if (e < E) {
       // all slices are loaded before the first add (clamped, always valid indices)
       const float* p0 = a.src + t * a.ld + e;
-      if (a.ks == 1) {
-        v = p0[0];
-      } else {
-        float u[kMaxSlices];
+      float u[KSM];
 #pragma unroll
-        for (int q = 0; q < kMaxSlices; ++q)
-          u[q] = p0[(q < a.ks ? q : a.ks - 1) * a.slice_stride];
-        v = u[0];
+      for (int q = 0; q < KSM; ++q) u[q] = p0[(q < a.ks ? q : a.ks - 1) * a.slice_stride];
+      v = u[0];
 #pragma unroll
-        for (int q = 1; q < kMaxSlices; ++q)
-          if (q < a.ks) v += u[q];
-      }
+      for (int q = 1; q < KSM; ++q)
+        if (q < a.ks) v += u[q];
       if (a.logits_out) a.logits_out[t * E + e] = v;
     }
     val[j] = v;
@@ -342,13 +341,26 @@ hipError_t launch_router_bf16(const void* x, const void* w_router, const void* w
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.T <= 0) return hipSuccess;
+  if (a.ks < 1 || a.ks > kMaxSlices) return hipErrorInvalidValue;
   dim3 g((unsigned)((a.T + 3) / 4)), b(256);
   const int npl = (a.E + 63) / 64;
-#define MOE_TOPK_CASE(N)                                              \
-  case N:                                                             \
-    hipLaunchKernelGGL(topk_kernel<N>, g, b, 0, stream, a);           \
-    break;
+  if (npl < 1 || npl > 16) return hipErrorInvalidValue;
+  const auto go = [&](auto n) {
+    constexpr int N = decltype(n)::value;
+    if (a.ks == 1)
+      hipLaunchKernelGGL((topk_kernel<N, 1>), g, b, 0, stream, a);
+    else if (a.ks == 2)
+      hipLaunchKernelGGL((topk_kernel<N, 2>), g, b, 0, stream, a);
+    else if (a.ks <= 4)
+      hipLaunchKernelGGL((topk_kernel<N, 4>), g, b, 0, stream, a);
+    else
+      hipLaunchKernelGGL((topk_kernel<N, 8>), g, b, 0, stream, a);
+  };
   switch (npl) {
+#define MOE_TOPK_CASE(N) \
+  case N:                \
+    go(std::integral_constant<int, N>{}); \
+    break;
     MOE_TOPK_CASE(1)
     MOE_TOPK_CASE(2)
     MOE_TOPK_CASE(3)
@@ -365,10 +377,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     MOE_TOPK_CASE(14)
     MOE_TOPK_CASE(15)
     MOE_TOPK_CASE(16)
-    default:
-      return hipErrorInvalidValue;
-  }
 #undef MOE_TOPK_CASE
+  }
   return hipGetLastError();
 }
 
