@@ -171,14 +171,19 @@ __global__ void __launch_bounds__(kSSThreads) scan_scatter_kernel(
   for (int e = threadIdx.x; e < E; e += kSSThreads) {
     int acc = 0;
     for (int64_t s0 = 0; s0 < nseg; s0 += kSSBatch) {
+      // the batch's loads go out together: clamped rows (always valid), no branch between
+      // them (a conditional load would sit in its own block and wait for the previous one)
       int v[kSSBatch];
 #pragma unroll
-      for (int u = 0; u < kSSBatch; ++u) v[u] = s0 + u < nseg ? seg_counts[(s0 + u) * E + e] : 0;
+      for (int u = 0; u < kSSBatch; ++u) {
+        const int64_t sg = s0 + u < nseg ? s0 + u : nseg - 1;
+        v[u] = seg_counts[sg * E + e];
+      }
 #pragma unroll
       for (int u = 0; u < kSSBatch; ++u) {
         const int64_t sg = s0 + u;
         if (sg >= seg0 && sg < seg0 + kSSWaves) run[(sg - seg0) * E + e] = acc;
-        acc += v[u];
+        acc += sg < nseg ? v[u] : 0;
       }
     }
     cnt[e] = acc < cap ? acc : cap;
@@ -232,10 +237,10 @@ __global__ void __launch_bounds__(kSSThreads) scan_scatter_kernel(
     }
     if (valid) {
       const int rank = __popcll(peers & lt);
-      const int base = r[e];
+      const int base = r[e], first = off[e];  // both LDS reads in flight together
       const int q = base + rank;  // rank of this assignment within its expert
       if (q < cap) {
-        const int pos = off[e] + q;
+        const int pos = first + q;
         perm[pos] = (int32_t)a;
         inv_perm[a] = pos;
       } else {
@@ -336,10 +341,10 @@ __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
       }
       if (valid) {
         const int rank = __popcll(peers & lt);
-        const int base = h[e];
+        const int base = h[e], first = off[e];  // both LDS reads in flight together
         const int q = base + rank;  // rank within the expert
         if (q < cap) {
-          const int pos = off[e] + q;
+          const int pos = first + q;
           perm[pos] = (int32_t)a;
           inv_perm[a] = pos;
         } else {
