@@ -157,6 +157,40 @@ def test_router_gemm_and_topk(name, T):
         assert np.all(np.abs(f64(r["shared_gate"]) - want_g) <= gbound)
 
 
+@pytest.mark.parametrize("T,D,E,K,scoring,gated,bias", [(8200, 1024, 300, 5, "softmax", True, True),
+                                                       (8192, 512, 1024, 8, "sigmoid", False, False)])
+def test_matrix_core_router_partial_column_tiles(T, D, E, K, scoring, gated, bias):
+    """The matrix-core router where E is not a multiple of its 256-column tiles: E = 300 (a
+    second, mostly empty column tile, with a logit bias and the gate logit from the top-K
+    kernel; 2 slices) and E = 1024 (four column tiles; top-K over 16 logits per lane)."""
+    g = torch.Generator(device="cpu").manual_seed(E)
+    x = torch.randn((T, D), generator=g).to(torch.bfloat16)
+    wr = (torch.randn((E, D), generator=g) * D ** -0.5).to(torch.bfloat16)
+    ws = (torch.randn((1, D), generator=g) * 0.02).to(torch.bfloat16) if gated else None
+    lb = torch.randn(E, generator=g) * 0.5 if bias else None
+    p = abi.make_problem(T=T, D=D, E=E, K=K, F=64, F_shared=64 if gated else 0,
+                         shared_gated=gated, scoring=scoring)
+    plan = abi.describe_plan(p)
+    assert plan.startswith("router: mfma 256x256"), plan
+    r = abi.alloc_routing(p, DEV)
+    weights = {"w_router": wr.to(DEV), "logit_bias": None if lb is None else lb.to(DEV),
+               "ws_gate": None if ws is None else ws.to(DEV)}
+    abi.moe_route(p, x.to(DEV), weights, r, abi.alloc_workspace(p, DEV))
+    torch.cuda.synchronize()
+    X, W = f64(x), f64(wr)
+    want_logits = O.router_logits(X, W, f64(lb))
+    got_logits = f64(r["logits"])
+    assert np.all(np.abs(got_logits - want_logits) <= _fp32_logit_bound(X, W, want_logits))
+    want_idx = O.topk_select(got_logits, K)
+    np.testing.assert_array_equal(i64(r["topk_idx"]), want_idx)
+    np.testing.assert_allclose(f64(r["topk_w"]), O.routing_weights(got_logits, want_idx, scoring),
+                               rtol=0, atol=TOL_ROUTING_W)
+    if gated:
+        Ws = f64(ws)
+        gbound = 0.25 * _fp32_logit_bound(X, Ws, X @ Ws.T)[:, 0] + 1e-7
+        assert np.all(np.abs(f64(r["shared_gate"]) - O.shared_gate(X, Ws)) <= gbound)
+
+
 # ---- selection-only bias ("1.6 ..." §三): choose on score + bias, weight with the score ----
 
 def select_key_bound(logits64, bias64, scoring, E):
