@@ -242,7 +242,10 @@ Layout layout(const moe_problem* p) {
   L.offsets = take((size_t)(E + 1) * 4);
   L.perm = take((size_t)A * 4);
   L.inv_perm = take((size_t)A * 4);
-  L.seg_counts = take((size_t)moe::dispatch_num_segments(A) * E * 4);
+  {  // per-segment histograms, then their sums per chunk of 4 segments
+    const size_t nseg = (size_t)moe::dispatch_num_segments(A);
+    L.seg_counts = take((nseg + (nseg + 3) / 4) * E * 4);
+  }
   L.tiles = take((size_t)L.max_mtiles * moe::kTileStride * 4);
   L.tile_count = take(16);
   L.H = take((size_t)A * p->F * es);

@@ -64,30 +64,44 @@ __device__ int block_exclusive_scan(int v, int* scratch /* >= NT / 64 + 1 ints *
   return r;
 }
 
+// Work-group b counts segments 4 b .. 4 b + 3 (one per wave) and also writes their sum, the
+// histogram of chunk b (kChunkSegs segments), so that the scatter work-groups can form the
+// counts of all earlier segments from a quarter as many rows.
+constexpr int kChunkSegs = 4;
+
 __global__ void __launch_bounds__(256) count_kernel(const int32_t* __restrict__ idx, int64_t A,
                                                     int E, int64_t nseg,
-                                                    int32_t* __restrict__ seg_counts) {
+                                                    int32_t* __restrict__ seg_counts,
+                                                    int32_t* __restrict__ chunk_counts) {
   extern __shared__ int hist_all[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t seg = (int64_t)blockIdx.x * 4 + wave;
-  if (seg >= nseg) return;  // whole wave; no block-wide barrier below
+  const int64_t seg = (int64_t)blockIdx.x * kChunkSegs + wave;
   int* hist = hist_all + wave * E;
   for (int e = lane; e < E; e += 64) hist[e] = 0;
-  const int64_t a0 = seg * kSegLen;
-  int ev[kSegRounds];
+  if (seg < nseg) {  // whole wave
+    const int64_t a0 = seg * kSegLen;
+    int ev[kSegRounds];
 #pragma unroll
-  for (int r = 0; r < kSegRounds; ++r) {
-    const int64_t a = a0 + r * 64 + lane;
-    ev[r] = a < A ? idx[a] : -1;
+    for (int r = 0; r < kSegRounds; ++r) {
+      const int64_t a = a0 + r * 64 + lane;
+      ev[r] = a < A ? idx[a] : -1;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int r = 0; r < kSegRounds; ++r)
+      if (ev[r] >= 0 && ev[r] < E) atomicAdd(&hist[ev[r]], 1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    for (int e = lane; e < E; e += 64) seg_counts[seg * E + e] = hist[e];
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int c = 0;
 #pragma unroll
-  for (int r = 0; r < kSegRounds; ++r)
-    if (ev[r] >= 0 && ev[r] < E) atomicAdd(&hist[ev[r]], 1);
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  for (int e = lane; e < E; e += 64) seg_counts[seg * E + e] = hist[e];
+    for (int w = 0; w < kChunkSegs; ++w) c += hist_all[w * E + e];
+    chunk_counts[(int64_t)blockIdx.x * E + e] = c;
+  }
 }
 
 // Builds the tile map from per-expert counts held in LDS.  One entry per M tile:
@@ -154,10 +168,12 @@ __global__ void __launch_bounds__(kScanThreads) tile_map_kernel(const int32_t* _
 constexpr int kSSThreads = 512;
 constexpr int kSSWaves = kSSThreads / 64;
 constexpr int kSSBatch = 64;  // histogram rows loaded together
+static_assert(kSSWaves % kChunkSegs == 0, "a scatter work-group owns whole count chunks");
 
 __global__ void __launch_bounds__(kSSThreads) scan_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t A, int E, int nbits, int cap, int64_t nseg,
-    const int32_t* __restrict__ seg_counts, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ seg_counts, const int32_t* __restrict__ chunk_counts,
+    int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
     const int bm, int32_t* __restrict__ tiles, int32_t* __restrict__ tile_count) {
   extern __shared__ int sm[];
@@ -168,23 +184,38 @@ __global__ void __launch_bounds__(kSSThreads) scan_scatter_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t seg0 = (int64_t)blockIdx.x * kSSWaves;
 
+  // per expert: the count of every chunk (their sum is the expert's total; the chunks before
+  // this work-group's first give the count of all earlier segments), then this work-group's own
+  // segments one by one.  Loads go out a batch at a time: clamped rows, no branch between them.
+  const int64_t nchunk = (nseg + kChunkSegs - 1) / kChunkSegs;
+  const int64_t chunk0 = seg0 / kChunkSegs;  // kSSWaves is a multiple of kChunkSegs
   for (int e = threadIdx.x; e < E; e += kSSThreads) {
-    int acc = 0;
-    for (int64_t s0 = 0; s0 < nseg; s0 += kSSBatch) {
-      // the batch's loads go out together: clamped rows (always valid), no branch between
-      // them (a conditional load would sit in its own block and wait for the previous one)
+    int acc = 0, before = 0;
+    for (int64_t c0 = 0; c0 < nchunk; c0 += kSSBatch) {
       int v[kSSBatch];
 #pragma unroll
       for (int u = 0; u < kSSBatch; ++u) {
-        const int64_t sg = s0 + u < nseg ? s0 + u : nseg - 1;
-        v[u] = seg_counts[sg * E + e];
+        const int64_t c = c0 + u < nchunk ? c0 + u : nchunk - 1;
+        v[u] = chunk_counts[c * E + e];
       }
 #pragma unroll
       for (int u = 0; u < kSSBatch; ++u) {
-        const int64_t sg = s0 + u;
-        if (sg >= seg0 && sg < seg0 + kSSWaves) run[(sg - seg0) * E + e] = acc;
-        acc += sg < nseg ? v[u] : 0;
+        const int64_t c = c0 + u;
+        const int x = c < nchunk ? v[u] : 0;
+        acc += x;
+        if (c < chunk0) before += x;
       }
+    }
+    int own[kSSWaves];
+#pragma unroll
+    for (int w = 0; w < kSSWaves; ++w) {
+      const int64_t sg = seg0 + w < nseg ? seg0 + w : nseg - 1;
+      own[w] = seg_counts[sg * E + e];
+    }
+#pragma unroll
+    for (int w = 0; w < kSSWaves; ++w) {
+      if (seg0 + w < nseg) run[w * E + e] = before;
+      before += seg0 + w < nseg ? own[w] : 0;
     }
     cnt[e] = acc < cap ? acc : cap;
   }
@@ -404,13 +435,15 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_co
   }
   const dim3 g((unsigned)((nseg + 3) / 4)), b(256);
   hipLaunchKernelGGL(count_kernel, g, b, (size_t)4 * E * sizeof(int), stream, idx, A, E, nseg,
-                     seg_counts);
+                     seg_counts, seg_counts + nseg * E);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const size_t lds = (size_t)((kSSWaves + 2) * E + 32) * sizeof(int);
   const unsigned groups = (unsigned)((nseg + kSSWaves - 1) / kSSWaves) + (tiles ? 1 : 0);
-  hipLaunchKernelGGL(scan_scatter_kernel, dim3(groups), dim3(kSSThreads), lds, stream, idx, A, E, nbits, cap, nseg, seg_counts,
-                     counts, offsets, perm, inv_perm, bm, tiles, tile_count);
+  const int32_t* chunk_counts = seg_counts + nseg * E;
+  hipLaunchKernelGGL(scan_scatter_kernel, dim3(groups), dim3(kSSThreads), lds, stream, idx, A, E,
+                     nbits, cap, nseg, seg_counts, chunk_counts, counts, offsets, perm, inv_perm,
+                     bm, tiles, tile_count);
   return hipGetLastError();
 }
 
