@@ -30,38 +30,45 @@ constexpr int kSegLen = 64 * kSegRounds;      // assignments per segment (one wa
 constexpr int64_t kFusedMaxA = 8192;
 constexpr int kFusedMaxE = kDispatchOneWgMaxE;
 
-__device__ __forceinline__ int wave_prefix_exclusive(int v, int lane) {
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+// One DPP step of a wave-wide inclusive sum: v plus the value CTRL brings from another lane;
+// lanes with no source under CTRL, or in rows outside ROW_MASK, add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int add_dpp(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Exclusive prefix sum over the wave's 64 lanes (lane order): shifts by 1, 2, 4 and 8 lanes
+// within each row of 16, then the last lane of row 0 carried into rows 1 and 3 and that of
+// row 1 into rows 2 and 3 (integer adds, so the grouping does not change the result).
+__device__ __forceinline__ int wave_prefix_exclusive(int v) {
+  int x = add_dpp<0x111, 0xf>(v);  // row_shr:1
+  x = add_dpp<0x112, 0xf>(x);      // row_shr:2
+  x = add_dpp<0x114, 0xf>(x);      // row_shr:4
+  x = add_dpp<0x118, 0xf>(x);      // row_shr:8
+  x = add_dpp<0x142, 0xa>(x);      // row_bcast:15 into rows 1 and 3
+  x = add_dpp<0x143, 0xc>(x);      // row_bcast:31 into rows 2 and 3
   return x - v;
 }
 
 // Exclusive scan of one int per thread across an NT-thread block.  Returns the prefix and
-// writes the block total to *total.
+// writes the block total to *total.  Every thread adds up the wave totals itself (the same
+// LDS words for the whole wave), so no thread scans them for the others.
 template <int NT>
-__device__ int block_exclusive_scan(int v, int* scratch /* >= NT / 64 + 1 ints */, int* total) {
+__device__ int block_exclusive_scan(int v, int* scratch /* >= NT / 64 ints */, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ex = wave_prefix_exclusive(v, lane);
+  const int ex = wave_prefix_exclusive(v);
   if (lane == 63) scratch[wave] = ex + v;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < NT / 64; ++w) {
-      const int c = scratch[w];
-      scratch[w] = run;
-      run += c;
-    }
-    scratch[NT / 64] = run;
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int c = scratch[w];
+    all += c;
+    before += w < wave ? c : 0;
   }
-  __syncthreads();
-  const int r = ex + scratch[wave];
-  *total = scratch[NT / 64];
-  __syncthreads();
-  return r;
+  *total = all;
+  __syncthreads();  // scratch is free for the next scan
+  return ex + before;
 }
 
 // Work-group b counts segments 4 b .. 4 b + 3 (one per wave) and also writes their sum, the
@@ -325,11 +332,14 @@ __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
   __syncthreads();
   // per expert: each wave's first position within the expert, and the expert's count
   for (int e = threadIdx.x; e < E; e += kScanThreads) {
+    int c[kFusedWaves];  // every wave's count read before the first running rank is written
+#pragma unroll
+    for (int w = 0; w < kFusedWaves; ++w) c[w] = hist[w * E + e];
     int run = 0;
+#pragma unroll
     for (int w = 0; w < kFusedWaves; ++w) {
-      const int c = hist[w * E + e];
       hist[w * E + e] = run;
-      run += c;
+      run += c[w];
     }
     cnt[e] = run < cap ? run : cap;  // rows kept
   }
