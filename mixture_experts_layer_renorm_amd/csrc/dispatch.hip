@@ -264,6 +264,7 @@ __global__ void __launch_bounds__(kSSThreads) scan_scatter_kernel(
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int rd = 0; rd < kSegRounds; ++rd) {
+    if (a0 + rd * 64 >= A) break;  // uniform: the rest of a short last segment is empty
     const int64_t a = a0 + rd * 64 + lane;
     const int e = ev[rd];
     const bool valid = e >= 0 && e < E;
@@ -371,6 +372,7 @@ __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
     }
 #pragma unroll
     for (int r = 0; r < kFusedBatch; ++r) {
+      if (b0 + r * 64 >= a_end) break;  // uniform: no id of this wave's range is left
       const int64_t a = b0 + r * 64 + lane;
       const int e = ev[r];
       const bool valid = e >= 0 && e < E;
