@@ -26,7 +26,7 @@ namespace {
 constexpr int kScanThreads = 1024;
 constexpr int kSegRounds = 8;                // 64-id rounds per segment
 constexpr int kSegLen = 64 * kSegRounds;      // assignments per segment (one wave)
-// Single-work-group dispatch up to this many assignments (its LDS holds 18 ints per expert).
+// Single-work-group dispatch up to this many assignments (its LDS holds 17 ints per expert).
 constexpr int64_t kFusedMaxA = 8192;
 constexpr int kFusedMaxE = kDispatchOneWgMaxE;
 
@@ -69,6 +69,35 @@ __device__ int block_exclusive_scan(int v, int* scratch /* >= NT / 64 ints */, i
   *total = all;
   __syncthreads();  // scratch is free for the next scan
   return ex + before;
+}
+
+// Two exclusive scans of one int each per thread across an NT-thread block, with one pair of
+// barriers: *pv, *pu the prefixes of v and u, *tv, *tu their block totals.
+template <int NT>
+__device__ void block_exclusive_scan2(int v, int u, int* scratch /* >= 2 NT / 64 ints */, int* pv,
+                                      int* pu, int* tv, int* tu) {
+  constexpr int W = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ev = wave_prefix_exclusive(v), eu = wave_prefix_exclusive(u);
+  if (lane == 63) {
+    scratch[wave] = ev + v;
+    scratch[W + wave] = eu + u;
+  }
+  __syncthreads();
+  int bv = 0, bu = 0, av = 0, au = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const int cv = scratch[w], cu = scratch[W + w];
+    av += cv;
+    au += cu;
+    bv += w < wave ? cv : 0;
+    bu += w < wave ? cu : 0;
+  }
+  *pv = ev + bv;
+  *pu = eu + bu;
+  *tv = av;
+  *tu = au;
+  __syncthreads();  // scratch is free again
 }
 
 // Work-group b counts segments 4 b .. 4 b + 3 (one per wave) and also writes their sum, the
@@ -120,6 +149,23 @@ __global__ void __launch_bounds__(256) count_kernel(const int32_t* __restrict__ 
 // (390 rows as 224 + 166, 13 pairs, not 195 + 195, 14 pairs) saves MFMAs but lets the tiles
 // drift by a pair in seven: measured on MI355X it made the sigmoid layer's grouped GEMMs 24%
 // slower.
+// The map entries of expert e: c rows from position off, in mt M tiles from map index first.
+__device__ __forceinline__ void write_tiles(int e, int c, int mt, int first, int off,
+                                            int32_t* tiles) {
+  const int base_rows = mt > 0 ? c / mt : 0, extra = mt > 0 ? c % mt : 0;
+  for (int q = 0; q < mt; ++q) {
+    int32_t* ent = tiles + (int64_t)(first + q) * kTileStride;
+    ent[0] = e;
+    ent[1] = off + q * base_rows + min(q, extra);
+    ent[2] = base_rows + (q < extra ? 1 : 0);
+    ent[3] = 0;
+    ent[4] = first;
+    ent[5] = mt;
+    ent[6] = 0;
+    ent[7] = 0;
+  }
+}
+
 template <int NT>
 __device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, int bm, int* scratch,
                             int32_t* tiles, int32_t* tile_count) {
@@ -130,18 +176,7 @@ __device__ void build_tiles(const int* cnt_lds, const int* off_lds, int E, int b
     const int mt = (c + bm - 1) / bm;
     int chunk_total;
     const int first = block_exclusive_scan<NT>(mt, scratch, &chunk_total) + total;
-    const int base_rows = mt > 0 ? c / mt : 0, extra = mt > 0 ? c % mt : 0;
-    for (int q = 0; q < mt; ++q) {
-      int32_t* ent = tiles + (int64_t)(first + q) * kTileStride;
-      ent[0] = e;
-      ent[1] = off_lds[e] + q * base_rows + min(q, extra);
-      ent[2] = base_rows + (q < extra ? 1 : 0);
-      ent[3] = 0;
-      ent[4] = first;
-      ent[5] = mt;
-      ent[6] = 0;
-      ent[7] = 0;
-    }
+    if (e < E) write_tiles(e, c, mt, first, off_lds[e], tiles);
     total += chunk_total;
   }
   if (threadIdx.x == 0) tile_count[0] = total;
@@ -302,6 +337,10 @@ __global__ void __launch_bounds__(kSSThreads) scan_scatter_kernel(
 constexpr int kFusedWaves = kScanThreads / 64;
 constexpr int kFusedBatch = 8;  // 64-id rounds whose loads are issued together
 
+static_assert(kFusedMaxA <= (int64_t)kFusedWaves * 64 * kFusedBatch,
+              "automatic one-work-group batches fit one batch of ids per wave");
+static_assert(kFusedMaxE <= kScanThreads, "one expert per thread in the scans");
+
 __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
     const int32_t* __restrict__ idx, int64_t A, int E, int nbits, int cap,
     int32_t* __restrict__ counts,
@@ -309,30 +348,42 @@ __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
     const int bm, int32_t* __restrict__ tiles, int32_t* __restrict__ tile_count) {
   extern __shared__ int sm[];
   int* hist = sm;                       // [kFusedWaves][E]: counts, then running ranks
-  int* cnt = hist + kFusedWaves * E;    // [E]
-  int* off = cnt + E;                   // [E]
-  int* scratch = off + E;               // [32]
+  int* off = hist + kFusedWaves * E;    // [E]
+  int* scratch = off + E;               // [2 kFusedWaves]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t L = ((A + kFusedWaves - 1) / kFusedWaves + 63) / 64 * 64;
   const int64_t a_begin = wave * L, a_end = min(A, a_begin + L);
-  int* h = hist + wave * E;
-  for (int e = lane; e < E; e += 64) h[e] = 0;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  for (int64_t b0 = a_begin; b0 < a_end; b0 += 64 * kFusedBatch) {
-    int ev[kFusedBatch];
+  // The wave's ids, a batch of 64 * kFusedBatch at a time; the first batch is requested before
+  // anything else.  When a wave's range is one batch (always, unless this path is forced for a
+  // larger batch), the scatter reuses it instead of loading the ids again.
+  const bool one_batch = L <= 64 * kFusedBatch;  // the same for every wave
+  int ev[kFusedBatch];
+  const auto load_ids = [&](int64_t b0) {
 #pragma unroll
     for (int r = 0; r < kFusedBatch; ++r) {
       const int64_t a = b0 + r * 64 + lane;
       ev[r] = a < a_end ? idx[a] : -1;
     }
+  };
+  load_ids(a_begin);
+  int* h = hist + wave * E;
+  for (int e = lane; e < E; e += 64) h[e] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  for (int64_t b0 = a_begin;;) {
 #pragma unroll
     for (int r = 0; r < kFusedBatch; ++r)
       if (ev[r] >= 0 && ev[r] < E) atomicAdd(&h[ev[r]], 1);
+    b0 += 64 * kFusedBatch;
+    if (b0 >= a_end) break;
+    load_ids(b0);
   }
   __syncthreads();
-  // per expert: each wave's first position within the expert, and the expert's count
-  for (int e = threadIdx.x; e < E; e += kScanThreads) {
+  // thread e: each wave's first position within expert e, the rows it keeps, their M tiles;
+  // then the expert offsets and the tile map's first entries in one pair of scans
+  const int e = threadIdx.x;
+  int kept = 0;
+  if (e < E) {
     int c[kFusedWaves];  // every wave's count read before the first running rank is written
 #pragma unroll
     for (int w = 0; w < kFusedWaves; ++w) c[w] = hist[w * E + e];
@@ -342,49 +393,41 @@ __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
       hist[w * E + e] = run;
       run += c[w];
     }
-    cnt[e] = run < cap ? run : cap;  // rows kept
+    kept = run < cap ? run : cap;
   }
-  __syncthreads();
-  int total = 0;
-  for (int base = 0; base < E; base += kScanThreads) {
-    const int ee = base + threadIdx.x;
-    const int v = ee < E ? cnt[ee] : 0;
-    int chunk_total;
-    const int ex = block_exclusive_scan<kScanThreads>(v, scratch, &chunk_total) + total;
-    if (ee < E) {
-      off[ee] = ex;
-      counts[ee] = v;
-      offsets[ee] = ex;
-    }
-    total += chunk_total;
+  const int mt = tiles ? (kept + bm - 1) / bm : 0;
+  int first_row, first_tile, rows_total, tiles_total;
+  block_exclusive_scan2<kScanThreads>(kept, mt, scratch, &first_row, &first_tile, &rows_total,
+                                      &tiles_total);
+  if (e < E) {
+    off[e] = first_row;
+    counts[e] = kept;
+    offsets[e] = first_row;
+    if (tiles) write_tiles(e, kept, mt, first_tile, first_row, tiles);
   }
-  if (threadIdx.x == 0) offsets[E] = total;
-  __syncthreads();
-  if (tiles) build_tiles<kScanThreads>(cnt, off, E, bm, scratch, tiles, tile_count);
+  if (threadIdx.x == 0) {
+    offsets[E] = rows_total;
+    if (tiles) tile_count[0] = tiles_total;
+  }
   __syncthreads();
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t b0 = a_begin; b0 < a_end; b0 += 64 * kFusedBatch) {
-    int ev[kFusedBatch];
-#pragma unroll
-    for (int r = 0; r < kFusedBatch; ++r) {
-      const int64_t a = b0 + r * 64 + lane;
-      ev[r] = a < a_end ? idx[a] : -1;
-    }
+    if (!one_batch) load_ids(b0);
 #pragma unroll
     for (int r = 0; r < kFusedBatch; ++r) {
       if (b0 + r * 64 >= a_end) break;  // uniform: no id of this wave's range is left
       const int64_t a = b0 + r * 64 + lane;
-      const int e = ev[r];
-      const bool valid = e >= 0 && e < E;
+      const int ee = ev[r];
+      const bool valid = ee >= 0 && ee < E;
       unsigned long long peers = __ballot(valid);
       for (int b = 0; b < nbits; ++b) {
-        const bool bit = (e >> b) & 1;
+        const bool bit = (ee >> b) & 1;
         const unsigned long long m = __ballot(bit);
         peers &= bit ? m : ~m;
       }
       if (valid) {
         const int rank = __popcll(peers & lt);
-        const int base = h[e], first = off[e];  // both LDS reads in flight together
+        const int base = h[ee], first = off[ee];  // both LDS reads in flight together
         const int q = base + rank;  // rank within the expert
         if (q < cap) {
           const int pos = first + q;
@@ -393,7 +436,7 @@ __global__ void __launch_bounds__(kScanThreads) dispatch_fused_kernel(
         } else {
           inv_perm[a] = -1;  // over capacity: dropped
         }
-        if (rank == 0) h[e] = base + __popcll(peers);
+        if (rank == 0) h[ee] = base + __popcll(peers);
       } else if (a < a_end) {
         inv_perm[a] = -1;
       }
@@ -440,7 +483,7 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t A, int E, int32_t* seg_co
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
   if (dispatch_fused(A, E, path)) {
-    const size_t lds = (size_t)((kFusedWaves + 2) * E + 32) * sizeof(int);
+    const size_t lds = (size_t)((kFusedWaves + 1) * E + 2 * kFusedWaves) * sizeof(int);
     hipLaunchKernelGGL(dispatch_fused_kernel, dim3(1), dim3(kScanThreads), lds, stream, idx, A,
                        E, nbits, cap, counts, offsets, perm, inv_perm, bm, tiles, tile_count);
     return hipGetLastError();
