@@ -92,10 +92,14 @@ def test_dispatch_deterministic():
 
 
 # Both dispatch implementations (one work-group for small batches; count/scan/scatter kernels
-# otherwise) forced on the same inputs, inside and outside their default ranges.
+# otherwise) forced on the same inputs, inside and outside their default ranges.  The
+# multi-kernel path cuts the assignments into segments of 128, 256 or 512 ids by batch size:
+# T*K = 32768 (128), 48000 and 65536 (256, the second at the bound of 256 segments), 65544 and
+# 1.28 M (512), each with a short last segment where T*K allows one.
 @pytest.mark.parametrize("path", ["one_workgroup", "multi"])
 @pytest.mark.parametrize("T,E,K", [(1, 1, 1), (64, 256, 8), (1023, 7, 3), (4096, 256, 8),
-                                   (2000, 768, 9), (20000, 64, 64)])
+                                   (2000, 768, 9), (6000, 256, 8), (8192, 320, 8),
+                                   (8193, 256, 8), (20000, 64, 64)])
 def test_dispatch_both_paths(path, T, E, K):
     g = torch.Generator().manual_seed(100 + T + E + K)
     idx = _topk_like(T, E, K, g)
