@@ -128,7 +128,7 @@ hipError_t launch_router_bf16(const void* x, const void* w_router, const void* w
 
 // Dispatch.  path: 0 = automatic, 1 = one work-group, 2 = count then scan + scatter (the
 // moe_dispatch_kernel values).
-constexpr int kDispatchOneWgMaxE = 768;  // LDS of the one-work-group kernel: 18 ints per expert
+constexpr int kDispatchOneWgMaxE = 768;  // LDS of the one-work-group kernel: 17 ints per expert
 int dispatch_segment_len(int64_t A);
 int64_t dispatch_num_segments(int64_t A);
 bool dispatch_supported(int E, int path);
