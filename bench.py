@@ -373,7 +373,7 @@ def cpu_baseline(cfg, layer, min_seconds, chunk):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} requested, but this build measures one GPU only "
+        print(f"bench.py: --gpus {args.gpus} requested, but this benchmark measures one GPU only "
               "(no sharding or collectives are built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
